@@ -1,0 +1,190 @@
+/*
+ * ufp4.h -- C ABI of libufp4.so, the MI355X (gfx950) hot path of the UFP4
+ * 4-bit training recipe: a fused random-Hadamard-transform + blockwise absmax
+ * 4-bit quantizer and the block-scaled 4-bit GEMMs it feeds.
+ *
+ * What is computed comes from "Rethinking Shrinkage Bias in LLM FP4
+ * Pretraining: Geometric Origin, Systemic Impact, and UFP4 Recipe"
+ * (arXiv 2606.20381), as summarised on paperlayer.ai:
+ *   - section 2 "Blockwise quantization": contiguous blocks, one shared scale
+ *     per block, a normalised codebook with largest magnitude gmax and a
+ *     rounding rule;
+ *   - section 2 "Rounding rules": RTNE (nearest level, deterministic ties) or
+ *     stochastic rounding between the adjacent levels (unbiased);
+ *   - section 2 "Random Hadamard transforms": random sign diagonal, then a
+ *     Sylvester Hadamard transform, applied along each training GEMM's
+ *     reduction dimension (input channels for FPROP, output channels for
+ *     DGRAD, tokens for WGRAD), the GEMM consuming the rotated quantized
+ *     operands;
+ *   - section 4 "UFP4 Recipe": uniform E1M2/INT4 grid, RHT on all three GEMMs,
+ *     stochastic rounding on dY only.
+ *
+ * Fixed choices where the pages are silent: block = RHT size = 16, FP32
+ * absmax block scale, one 16-bit sign mask per GEMM, Philox4x32-10 for the
+ * stochastic rounding, nibble layout sign<<3 | magnitude index, low nibble
+ * first.  Every quantized code and scale is bit-exact and deterministic;
+ * GEMM outputs are FP32 and deterministic run to run.
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are DEVICE pointers owned by the caller (the
+ *     library never allocates, frees or synchronises, and keeps no mutable
+ *     global state).  Descriptor structs are HOST memory read during the call.
+ *   - Work is enqueued on `stream` and runs asynchronously; results are valid
+ *     once the stream has reached that point.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns a negative status and enqueues nothing.  A HIP
+ *     launch failure returns UFP4_ERR_HIP.
+ *   - Inputs must be finite with |x| < 2^123 (larger values may overflow the
+ *     FP32 butterfly); NaN/Inf inputs give unspecified codes.
+ */
+#ifndef UFP4_H
+#define UFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  UFP4_OK = 0,
+  UFP4_ERR_INVALID_ARG = -1, /* null pointer, unknown enum, misalignment  */
+  UFP4_ERR_SHAPE = -2,       /* sizes inconsistent or out of range        */
+  UFP4_ERR_MISMATCH = -3,    /* GEMM operands quantized incompatibly      */
+  UFP4_ERR_UNSUPPORTED = -4, /* valid request this build does not serve   */
+  UFP4_ERR_HIP = -5          /* the HIP runtime rejected a launch         */
+} ufp4_status;
+
+/* Grids (paperlayer.ai summary, section 2 "FP4 formats").
+ *  UNIFORM: E1M2/INT4 grid {-7..7}/7 times the scale; the nibble's 3-bit
+ *           magnitude field is the integer level k (the E1M2 bit layout).
+ *  E2M1:    the OCP E2M1 grid {0,.5,1,1.5,2,3,4,6}/6 times the scale; the
+ *           nibble is the E2M1 bit pattern. */
+typedef enum { UFP4_GRID_UNIFORM = 0, UFP4_GRID_E2M1 = 1 } ufp4_grid;
+
+/* Rounding (paperlayer.ai summary, section 2 "Rounding rules").
+ *  RTNE: nearest level, ties to the even level index.
+ *  SR:   up with probability floor(f*2^32)/2^32, f the position between the
+ *        two adjacent levels; the 32 random bits of output element idx
+ *        (= row*kpad + k of the quantized layout) are word (idx & 3) of
+ *        Philox4x32-10 with key (seed lo, seed hi) and counter
+ *        (lo32(idx>>2), hi32(idx>>2), stream_id, 0). */
+typedef enum { UFP4_ROUND_RTNE = 0, UFP4_ROUND_SR = 1 } ufp4_round;
+
+/* Which input dimension the 16-element blocks run along.
+ *  ALONG_COLS: the contiguous dimension; output row i = input row i.
+ *  ALONG_ROWS: the strided dimension; the output is transposed (output row j
+ *              = input column j) and contiguous along the blocked dimension,
+ *              the K-contiguous layout every GEMM below consumes. */
+typedef enum { UFP4_BLOCKS_ALONG_COLS = 0, UFP4_BLOCKS_ALONG_ROWS = 1 } ufp4_axis;
+
+/* A quantized operand.  Caller-owned device buffers:
+ *   codes  [rows, kpad/2] bytes, byte j of a row = nib[2j] | nib[2j+1] << 4,
+ *          nibble = sign << 3 | magnitude index (a zero magnitude is always
+ *          nibble 0); 16-byte aligned.
+ *   scales [rows, kpad/16] FP32, the block absmax after the RHT (0 for an
+ *          all-zero block); 16-byte aligned.
+ * Layout is dense: row r's codes start at codes + r*kpad/2.
+ * `rows` and `kpad` describe the buffers and are set by the caller; the
+ * quantizer validates them and fills in k, grid, rht and sign_mask. */
+typedef struct {
+  uint8_t *codes;
+  float *scales;
+  int64_t rows;      /* output rows                                        */
+  int64_t k;         /* logical contraction length before padding          */
+  int64_t kpad;      /* padded contraction length, a multiple of 16        */
+  int32_t grid;      /* ufp4_grid                                          */
+  int32_t rht;       /* 1 if the 16-point RHT was applied                  */
+  uint32_t sign_mask;/* RHT signs: bit j set => d_j = -1 (bits 0..15 used) */
+  int32_t reserved;  /* must be 0                                          */
+} ufp4_qtensor;
+
+/* ufp4_rht_quantize -- fused RHT + blockwise absmax 4-bit quantization.
+ *
+ * x_bf16: device bf16 bit patterns [n_rows, n_cols] with row stride `ld`
+ *   elements (ld >= n_cols).  Any alignment works; 16-byte aligned x with ld
+ *   a multiple of 8 takes the vector-load path.
+ * axis: ufp4_axis.  ALONG_COLS: out->rows = n_rows, out->kpad =
+ *   roundup16(n_cols), zero-padded.  ALONG_ROWS: out->rows = n_cols, the
+ *   contraction runs over input rows.
+ * d_group_offsets / n_groups (ALONG_ROWS only; NULL and 0 otherwise): device
+ *   int64 [n_groups+1] non-decreasing row offsets, first 0, last n_rows, that
+ *   split the rows into groups (e.g. tokens per expert); every group is padded
+ *   to a multiple of 16 on its own, so no block straddles two groups, and
+ *   group e occupies columns [P_e, P_{e+1}) of the output with
+ *   P_e = sum_{e'<e} roundup16(count_e').  out->kpad must be at least
+ *   roundup16(n_rows + 15*n_groups); columns from P_{n_groups} to kpad are
+ *   written as zeros.  NULL means one group.  1 <= n_groups <= 4096.
+ * rht, sign_mask: apply y = (1/4) H16 D x per block (butterfly stages
+ *   h = 1,2,4,8 in FP32, then the exact 1/4) with D from the mask.
+ * grid, rnd, seed, stream_id: see the enums above (seed/stream_id ignored
+ *   for RTNE).
+ * Per block: s = max|y| (stored), r = RN(g/s) with g = 7 (uniform) or 6
+ *   (E2M1), t = RN(y*r) -- two roundings, no FMA; blocks with
+ *   0 < s < 2^-64 use y*2^64 and s*2^64 in that step (the stored scale is s).
+ * Returns UFP4_OK, INVALID_ARG (null pointer, bad enum, codes/scales not
+ *   16-byte aligned, reserved != 0), SHAPE (non-positive size, ld < n_cols,
+ *   rows/kpad not what the call produces), HIP. */
+ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols,
+                              int64_t ld, int32_t axis, const int64_t *d_group_offsets,
+                              int32_t n_groups, int32_t rht, uint32_t sign_mask,
+                              int32_t grid, int32_t rnd, uint64_t seed, uint32_t stream_id,
+                              ufp4_qtensor *out, hipStream_t stream);
+
+/* ufp4_dequantize -- out[r, k] for k < kpad, FP32 row-major with stride
+ * ld_out >= kpad:  (float)((double)(sign*L[idx]) * (double)s / g)  (the
+ * dequantized value of paperlayer.ai section 2 "Blockwise quantization").
+ * inverse_rht != 0 (requires q->rht): each block is mapped back through
+ * (1/4) D H16 in FP64 before the cast.  Returns OK, INVALID_ARG, SHAPE, HIP. */
+ufp4_status ufp4_dequantize(const ufp4_qtensor *q, int32_t inverse_rht, float *out,
+                            int64_t ld_out, hipStream_t stream);
+
+/* The three training GEMMs (paperlayer.ai section 2 "Random Hadamard
+ * transforms" and section 3.2).  All are C = A_hat * B_hat^T with both
+ * operands K-contiguous ("TN"), FP32 out, row-major with stride ldc >= N:
+ *   C[m, n] = sum_kb sa[m,kb] * sb[n,kb] * (sum_{k in kb} qa*qb) / g^2
+ * over the operands' common kpad.  Operands must agree on k, kpad, grid, rht
+ * and sign_mask (else UFP4_ERR_MISMATCH), which is what makes the rotation
+ * cancel.  Both grids are accepted.
+ *   FPROP: A = X  [T, H] (blocks along H), B = W   [F, H]  -> Y  [T, F]
+ *   DGRAD: A = dY [T, F] (blocks along F), B = W^T [H, F] (W quantized with
+ *          ALONG_ROWS) -> dX [T, H]
+ *   WGRAD: A = dY^T [F, T], B = X^T [H, T] (both ALONG_ROWS over tokens)
+ *          -> dW [F, H].  workspace may be NULL (workspace_bytes 0); a
+ *          workspace of ufp4_workspace_size(2, F, H, kpad, 1) bytes lets the
+ *          call split K across workgroups (deterministic fixed-order sum). */
+ufp4_status ufp4_gemm_fprop(const ufp4_qtensor *xq, const ufp4_qtensor *wq, float *y,
+                            int64_t ldy, hipStream_t stream);
+ufp4_status ufp4_gemm_dgrad(const ufp4_qtensor *dyq, const ufp4_qtensor *wtq, float *dx,
+                            int64_t ldx, hipStream_t stream);
+ufp4_status ufp4_gemm_wgrad(const ufp4_qtensor *dytq, const ufp4_qtensor *xtq, float *dw,
+                            int64_t lddw, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* ufp4_grouped_gemm -- the expert-grouped (MoE) form.
+ * kind 0 (FPROP) / 1 (DGRAD): rows of A are split into n_groups groups by the
+ *   device int64 offsets d_group_offsets[n_groups+1] (first 0, last a->rows);
+ *   B stacks the groups' operands, b->rows = n_groups * N; group e computes
+ *   C[off_e:off_{e+1}, :N] = A_e * B_e^T.  C is [a->rows, N], stride ldc.
+ * kind 2 (WGRAD): the contraction is split: A [M, kpad] and B [N, kpad] were
+ *   quantized ALONG_ROWS with the same offsets (per-group padding, see
+ *   ufp4_rht_quantize); C is [n_groups, M, N] with group stride M*ldc, and an
+ *   empty group writes zeros.
+ * workspace may be NULL.  Returns OK, INVALID_ARG, SHAPE, MISMATCH, HIP. */
+ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
+                              const ufp4_qtensor *a, const ufp4_qtensor *b, float *c,
+                              int64_t ldc, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Bytes of workspace a GEMM call can use to split K (0 if it never does). */
+size_t ufp4_workspace_size(int32_t kind, int64_t m, int64_t n, int64_t kpad, int32_t n_groups);
+
+/* Static, human-readable name of a status code. */
+const char *ufp4_status_string(ufp4_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UFP4_H */

@@ -269,8 +269,12 @@ _TINY = np.float32(2.0 ** -64)
 
 
 def quantize_blocked(xb: np.ndarray, rht: bool, sign_mask: int, grid: int,
-                     rnd: int, seed: int = 0, stream_id: int = 0):
+                     rnd: int, seed: int = 0, stream_id: int = 0, row_ids=None):
     """Quantize a [rows, K_p] float32 matrix along its last axis.
+
+    row_ids (optional) gives each row's index in the full quantized output,
+    so that a subset of rows draws the same SR random bits as in the full
+    tensor (SR index = row_id * K_p + k); default 0..rows-1.
 
     Returns (nibbles int64 [rows, K_p], scales float32 [rows, K_p/16]).
 
@@ -302,7 +306,10 @@ def quantize_blocked(xb: np.ndarray, rht: bool, sign_mask: int, grid: int,
     if rnd == ROUND_RTNE:
         idx = rtne_index(m, grid)
     else:
-        flat = np.arange(rows * kp, dtype=np.uint64).reshape(rows, kp // BLOCK, BLOCK)
+        rid = (np.arange(rows, dtype=np.uint64) if row_ids is None
+               else np.asarray(row_ids, dtype=np.uint64))
+        flat = (rid[:, None] * np.uint64(kp) +
+                np.arange(kp, dtype=np.uint64)[None, :]).reshape(rows, kp // BLOCK, BLOCK)
         u = sr_random_u32(flat, seed, stream_id)
         idx = sr_index(m, grid, u)
     neg = (t < 0)
@@ -326,16 +333,27 @@ def unpack_nibbles(codes: np.ndarray) -> np.ndarray:
 
 def quantize(x_bits: np.ndarray, axis: int, rht: bool, sign_mask: int,
              grid: int, rnd: int, seed: int = 0, stream_id: int = 0,
-             group_offsets=None):
+             group_offsets=None, kpad=None, out_rows=None):
     """Full quantizer on bf16 bit patterns [n_rows, n_cols].
 
     Returns (codes uint8 [rows, K_p/2], scales float32 [rows, K_p/16], K_p).
     SR element index = row * K_p + k in the quantized output's layout
     (reading).
+
+    kpad: a larger padded length than the minimum (columns beyond the data
+      are zero blocks), as a caller-sized buffer may have.
+    out_rows: evaluate only these output rows (indices into the full output);
+      with AXIS_COLS they are input rows, with AXIS_ROWS input columns.  The
+      codes equal those rows of the full result.
     """
     x = bf16_bits_to_f32(x_bits)
+    if out_rows is not None:
+        out_rows = np.asarray(out_rows, dtype=np.int64)
+        x = x[out_rows] if axis == AXIS_COLS else x[:, out_rows]
     xb = to_blocked_rows(x, axis, group_offsets)
-    nib, s = quantize_blocked(xb, rht, sign_mask, grid, rnd, seed, stream_id)
+    if kpad is not None and kpad > xb.shape[1]:
+        xb = np.concatenate([xb, np.zeros((xb.shape[0], kpad - xb.shape[1]), np.float32)], 1)
+    nib, s = quantize_blocked(xb, rht, sign_mask, grid, rnd, seed, stream_id, out_rows)
     return pack_nibbles(nib), s, xb.shape[1]
 
 

@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: libufp4.so loads, exports every function that
+include/ufp4.h declares, and rejects bad arguments on the host before
+enqueuing anything (so these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from uniform_grid_fp4_amd import ufp4 as U
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "ufp4.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:ufp4_status|size_t|const char \*)\s*(ufp4_\w+)\(",
+                                 src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    decl = declared_functions()
+    assert len(decl) == 8, decl
+    assert sorted(U.EXPORTS) == decl
+    L = U.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code, name in U.STATUS.items():
+        assert U.ufp4_status_string(code) == name
+    assert U.ufp4_status_string(12345) == "UFP4_ERR_UNKNOWN"
+
+
+def fake_desc(rows=32, k=32, kpad=32, grid=0, rht=1, mask=0x1234, codes=0x1000, scales=0x2000):
+    return U.QTensorDesc(codes, scales, rows, k, kpad, grid, rht, mask, 0)
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
+
+
+def quant(**kw):
+    a = dict(x=FAKE, n_rows=32, n_cols=32, ld=32, axis=0, goff=None, ng=0, rht=1, mask=0x1234,
+             grid=0, rnd=0, seed=1, sid=0, out=fake_desc())
+    a.update(kw)
+    return U.lib().ufp4_rht_quantize(a["x"], a["n_rows"], a["n_cols"], a["ld"], a["axis"],
+                                     a["goff"], a["ng"], a["rht"], a["mask"], a["grid"],
+                                     a["rnd"], a["seed"], a["sid"], ctypes.byref(a["out"]), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), -1),
+    (dict(out=fake_desc(codes=0)), -1),
+    (dict(out=fake_desc(codes=0x1008)), -1),        # codes not 16-byte aligned
+    (dict(axis=2), -1), (dict(grid=5), -1), (dict(rnd=2), -1), (dict(rht=3), -1),
+    (dict(mask=0x10000), -1),
+    (dict(n_rows=0), -2), (dict(n_cols=-1), -2), (dict(ld=16), -2),
+    (dict(out=fake_desc(kpad=48)), -2),             # row-wise kpad must be roundup16(n_cols)
+    (dict(out=fake_desc(rows=31)), -2),
+    (dict(goff=FAKE, ng=2), -1),                    # groups only for ALONG_ROWS
+    (dict(axis=1, goff=FAKE, ng=0), -1),
+    (dict(axis=1, goff=FAKE, ng=2000), -2),
+    (dict(axis=1, goff=FAKE, ng=2, out=fake_desc(kpad=32)), -2),  # needs >= roundup16(32+30)
+])
+def test_quantize_rejects(kw, expect):
+    assert quant(**kw) == expect
+
+
+def test_quantize_reserved_field_must_be_zero():
+    d = fake_desc()
+    d.reserved = 1
+    assert quant(out=d) == -1
+
+
+def gemm(fn, a, b, c=FAKE, ldc=32):
+    return fn(ctypes.byref(a), ctypes.byref(b), c, ldc, None)
+
+
+@pytest.mark.parametrize("name", ["ufp4_gemm_fprop", "ufp4_gemm_dgrad"])
+def test_gemm_validation(name):
+    fn = getattr(U.lib(), name)
+    ok = fake_desc()
+    assert gemm(fn, ok, fake_desc(k=16, kpad=16)) == -3        # K mismatch
+    assert gemm(fn, ok, fake_desc(grid=1)) == -3               # grid mismatch
+    assert gemm(fn, ok, fake_desc(rht=0)) == -3
+    assert gemm(fn, ok, fake_desc(mask=0x4321)) == -3          # rotation would not cancel
+    assert gemm(fn, ok, fake_desc(kpad=40)) == -2              # kpad % 16
+    assert gemm(fn, ok, fake_desc(rows=0)) == -2
+    assert gemm(fn, ok, fake_desc(scales=0x2004)) == -1        # misaligned
+    assert gemm(fn, ok, ok, c=None) == -1
+    assert gemm(fn, ok, fake_desc(rows=64), ldc=32) == -2      # ldc < N
+
+
+def test_wgrad_and_grouped_validation():
+    L = U.lib()
+    ok = fake_desc()
+    assert L.ufp4_gemm_wgrad(ctypes.byref(ok), ctypes.byref(ok), FAKE, 32, FAKE, 0, None) == -1
+    assert L.ufp4_gemm_wgrad(ctypes.byref(ok), ctypes.byref(fake_desc(grid=1)), FAKE, 32,
+                             None, 0, None) == -3
+    g = L.ufp4_grouped_gemm
+    assert g(3, 2, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 32, None, 0, None) == -1
+    assert g(0, 2, None, ctypes.byref(ok), ctypes.byref(ok), FAKE, 32, None, 0, None) == -1
+    assert g(0, 0, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 32, None, 0, None) == -2
+    assert g(0, 3, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 32, None, 0, None) == -2
+    assert g(2, 2, FAKE, ctypes.byref(ok), ctypes.byref(fake_desc(k=16, kpad=16)), FAKE, 32,
+             None, 0, None) == -3
+
+
+def test_dequantize_validation():
+    L = U.lib()
+    ok = fake_desc()
+    assert L.ufp4_dequantize(ctypes.byref(ok), 0, None, 32, None) == -1
+    assert L.ufp4_dequantize(ctypes.byref(ok), 0, FAKE, 16, None) == -2
+    assert L.ufp4_dequantize(ctypes.byref(fake_desc(rht=0)), 1, FAKE, 32, None) == -1
+    assert L.ufp4_dequantize(None, 0, FAKE, 32, None) == -1

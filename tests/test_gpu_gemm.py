@@ -1,0 +1,137 @@
+"""GPU parity of the block-scaled 4-bit GEMMs (dense FPROP/DGRAD/WGRAD and the
+expert-grouped forms) against the oracle's FP64 product of the dequantized
+operands, through the C ABI.  Bar: |C - C_ref| <= 1e-5 * sum_k |a_k||b_k| per
+output element.  Operands come from the GPU quantizer, whose bit-exactness is
+tested separately, and are read back for the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ufp4_oracle as O
+from uniform_grid_fp4_amd import ufp4 as U
+from uniform_grid_fp4_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-5
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def assert_close(C, ref, bound, what):
+    err = np.abs(C.astype(np.float64) - ref)
+    lim = TOL * bound
+    bad = err > lim
+    assert not bad.any(), (f"{what}: {bad.sum()} outside tolerance, worst ratio "
+                           f"{(err / np.maximum(lim, 1e-300)).max():.3g}")
+
+
+def rand_bf16(shape, seed, std=1.0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return (torch.randn(shape, device=DEV, generator=g) * std).to(torch.bfloat16)
+
+
+def qrow(x, mask, grid=U.GRID_UNIFORM, rnd=U.ROUND_RTNE, seed=0, sid=0):
+    return U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_COLS, True, mask, grid, rnd, seed, sid)
+
+
+def qcol(x, mask, grid=U.GRID_UNIFORM, rnd=U.ROUND_RTNE, seed=0, sid=0, goff=None):
+    gd = torch.as_tensor(goff, dtype=torch.int64, device=DEV) if goff is not None else None
+    return U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_ROWS, True, mask, grid, rnd, seed, sid, gd)
+
+
+def ref_gemm(a, b, grid=U.GRID_UNIFORM):
+    return O.gemm_tn(host(a.codes), host(a.scales), host(b.codes), host(b.scales), grid)
+
+
+@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+def test_tiny_layer_all_three_gemms(grid):
+    L = W.tiny(DEV)
+    mf, md, mw = L.masks
+    print(f"[gemm] tiny layer grid={grid}", flush=True)
+    xq, wq = qrow(L.x, mf, grid), qrow(L.w, mf, grid)
+    y = U.ufp4_gemm_fprop(xq, wq)
+    C, bnd = ref_gemm(xq, wq, grid)
+    assert_close(host(y), C, bnd, "fprop")
+    dyq = qrow(L.dy, md, grid, U.ROUND_SR, 1, 0)
+    wtq = qcol(L.w, md, grid)
+    dx = U.ufp4_gemm_dgrad(dyq, wtq)
+    C, bnd = ref_gemm(dyq, wtq, grid)
+    assert_close(host(dx), C, bnd, "dgrad")
+    dytq = qcol(L.dy, mw, grid, U.ROUND_SR, 1, 1)
+    xtq = qcol(L.x, mw, grid)
+    dw = U.ufp4_gemm_wgrad(dytq, xtq)
+    C, bnd = ref_gemm(dytq, xtq, grid)
+    assert_close(host(dw), C, bnd, "wgrad")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (130, 70, 48), (300, 200, 1040), (129, 257, 80),
+                                   (17, 384, 2000), (640, 128, 64)])
+def test_ragged_fprop(m, n, k):
+    print(f"[gemm] ragged {m}x{n}x{k}", flush=True)
+    a, b = rand_bf16((m, k), 1), rand_bf16((n, k), 2, 0.02)
+    aq, bq = qrow(a, 0xACE1), qrow(b, 0xACE1)
+    C, bnd = ref_gemm(aq, bq)
+    assert_close(host(U.ufp4_gemm_fprop(aq, bq)), C, bnd, "fprop")
+
+
+def test_output_stride_and_determinism():
+    a, b = rand_bf16((200, 96), 3), rand_bf16((150, 96), 4)
+    aq, bq = qrow(a, 7), qrow(b, 7)
+    big = torch.full((200, 160), 12345.0, device=DEV)
+    U.ufp4_gemm_fprop(aq, bq, out=big[:, 5:155])
+    C, bnd = ref_gemm(aq, bq)
+    h = host(big)
+    assert_close(h[:, 5:155], C, bnd, "strided")
+    assert (h[:, :5] == 12345.0).all() and (h[:, 155:] == 12345.0).all()
+    y1 = U.ufp4_gemm_fprop(aq, bq)
+    y2 = U.ufp4_gemm_fprop(aq, bq)
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("counts", [[5, 0, 17, 1, 0, 9], [0, 300, 0, 129, 128, 0, 1],
+                                    list(np.random.default_rng(4).integers(0, 70, size=40))])
+def test_grouped_fprop_dgrad(counts):
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T, H, F, E = int(off[-1]), 96, 80, len(counts)
+    print(f"[gemm] grouped fprop/dgrad E={E} T={T}", flush=True)
+    x = rand_bf16((T, H), 5)
+    w = rand_bf16((E * F, H), 6, 0.02)
+    dy = rand_bf16((T, F), 7, 1e-4)
+    offd = torch.as_tensor(off, device=DEV)
+    xq, wq = qrow(x, 0x1111), qrow(w, 0x1111)
+    y = U.ufp4_grouped_gemm(U.FPROP, offd, xq, wq)
+    C, bnd = O.grouped_gemm(0, off, host(xq.codes), host(xq.scales), host(wq.codes),
+                            host(wq.scales), F)
+    assert_close(host(y), C, bnd, "grouped fprop")
+    # DGRAD: B stacks each expert's W_e^T [H, F]
+    wt = torch.cat([w[e * F:(e + 1) * F].t().contiguous() for e in range(E)], 0)
+    wtq = qrow(wt, 0x2222)
+    dyq = qrow(dy, 0x2222, rnd=U.ROUND_SR, seed=3)
+    dx = U.ufp4_grouped_gemm(U.DGRAD, offd, dyq, wtq)
+    C, bnd = O.grouped_gemm(1, off, host(dyq.codes), host(dyq.scales), host(wtq.codes),
+                            host(wtq.scales), H)
+    assert_close(host(dx), C, bnd, "grouped dgrad")
+
+
+@pytest.mark.parametrize("counts", [[5, 0, 17, 16, 3], [0, 0, 500, 0], [1] * 20 + [0] * 5,
+                                    list(np.random.default_rng(5).integers(0, 300, size=12))])
+def test_grouped_wgrad(counts):
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T, H, F = int(off[-1]), 72, 136
+    print(f"[gemm] grouped wgrad E={len(counts)} T={T}", flush=True)
+    x = rand_bf16((T, H), 8)
+    dy = rand_bf16((T, F), 9, 1e-4)
+    dytq = qcol(dy, 0x3333, rnd=U.ROUND_SR, seed=4, sid=1, goff=off)
+    xtq = qcol(x, 0x3333, goff=off)
+    dw = U.ufp4_grouped_gemm(U.WGRAD, torch.as_tensor(off, device=DEV), dytq, xtq)
+    C, bnd = O.grouped_gemm(2, off, host(dytq.codes), host(dytq.scales), host(xtq.codes),
+                            host(xtq.scales), 0)
+    assert dw.shape == (len(counts), F, H)
+    assert_close(host(dw), C, bnd, "grouped wgrad")
+    for e, c in enumerate(counts):
+        if c == 0:
+            assert (host(dw[e]) == 0).all()

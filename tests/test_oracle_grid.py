@@ -187,3 +187,20 @@ def test_dequantize_values():
             lev = Fraction(O.LEVELS[grid][n & 7]).limit_denominator(4)
             exact = (-1 if n & 8 else 1) * lev * Fraction(float(scales[i, j // 16])) / int(O.GMAX[grid])
             assert float(v[i, j]) == float(np.float32(float(exact)))
+
+
+@pytest.mark.parametrize("axis", [O.AXIS_COLS, O.AXIS_ROWS])
+@pytest.mark.parametrize("rnd", [O.ROUND_RTNE, O.ROUND_SR])
+def test_row_subset_equals_rows_of_full_result(axis, rnd):
+    rng = np.random.default_rng(60)
+    x = rng.standard_normal((48, 40)).astype(np.float32)
+    b = (x.view(np.uint32) >> 16).astype(np.uint16)
+    cf, sf, kp = O.quantize(b, axis, True, 0x2468, O.GRID_UNIFORM, rnd, 9, 2)
+    rows = [0, 3, 17, cf.shape[0] - 1]
+    cs, ss, kp2 = O.quantize(b, axis, True, 0x2468, O.GRID_UNIFORM, rnd, 9, 2, out_rows=rows)
+    assert kp == kp2 and (cs == cf[rows]).all() and (ss == sf[rows]).all()
+    # a larger caller-sized kpad only appends zero blocks
+    ck, sk, kp3 = O.quantize(b, axis, True, 0x2468, O.GRID_UNIFORM, rnd, 9, 2, kpad=kp + 32)
+    assert kp3 == kp + 32 and (sk[:, -2:] == 0).all() and (ck[:, -16:] == 0).all()
+    if rnd == O.ROUND_RTNE:
+        assert (ck[:, :kp // 2] == cf).all()

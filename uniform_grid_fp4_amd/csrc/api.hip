@@ -1,0 +1,210 @@
+// C ABI of libufp4.so: host-side validation, then one launch on the caller's
+// stream.  No allocation, no synchronisation, no global mutable state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ufp4.h"
+#include "ufp4_kernels.h"
+
+using namespace ufp4;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t round_up16(int64_t n) { return (n + 15) / 16 * 16; }
+
+ufp4_status check_qtensor(const ufp4_qtensor *q) {
+  if (q == nullptr || q->codes == nullptr || q->scales == nullptr) return UFP4_ERR_INVALID_ARG;
+  if (!aligned16(q->codes) || !aligned16(q->scales) || q->reserved != 0)
+    return UFP4_ERR_INVALID_ARG;
+  if (q->grid != UFP4_GRID_UNIFORM && q->grid != UFP4_GRID_E2M1) return UFP4_ERR_INVALID_ARG;
+  if (q->rht != 0 && q->rht != 1) return UFP4_ERR_INVALID_ARG;
+  if (q->rows <= 0 || q->kpad <= 0 || q->kpad % 16 != 0 || q->k <= 0 || q->k > q->kpad)
+    return UFP4_ERR_SHAPE;
+  return UFP4_OK;
+}
+
+ufp4_status check_pair(const ufp4_qtensor *a, const ufp4_qtensor *b) {
+  ufp4_status s = check_qtensor(a);
+  if (s != UFP4_OK) return s;
+  s = check_qtensor(b);
+  if (s != UFP4_OK) return s;
+  if (a->k != b->k || a->kpad != b->kpad || a->grid != b->grid || a->rht != b->rht ||
+      (a->rht && ((a->sign_mask ^ b->sign_mask) & 0xFFFFu) != 0))
+    return UFP4_ERR_MISMATCH;
+  return UFP4_OK;
+}
+
+ufp4_status dense_gemm(const ufp4_qtensor *a, const ufp4_qtensor *b, float *c, int64_t ldc,
+                       hipStream_t stream) {
+  ufp4_status s = check_pair(a, b);
+  if (s != UFP4_OK) return s;
+  if (c == nullptr) return UFP4_ERR_INVALID_ARG;
+  if (ldc < b->rows) return UFP4_ERR_SHAPE;
+  GemmArgs g{};
+  g.a_codes = a->codes;
+  g.a_scales = a->scales;
+  g.b_codes = b->codes;
+  g.b_scales = b->scales;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.kpad = a->kpad;
+  g.c = c;
+  g.ldc = ldc;
+  g.mode = 0;
+  g.goff = nullptr;
+  g.n_groups = 1;
+  g.grid = a->grid;
+  return launch_gemm(g, stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
+                              int32_t axis, const int64_t *d_group_offsets, int32_t n_groups,
+                              int32_t rht, uint32_t sign_mask, int32_t grid, int32_t rnd,
+                              uint64_t seed, uint32_t stream_id, ufp4_qtensor *out,
+                              hipStream_t stream) {
+  if (x_bf16 == nullptr || out == nullptr || out->codes == nullptr || out->scales == nullptr)
+    return UFP4_ERR_INVALID_ARG;
+  if (!aligned16(out->codes) || !aligned16(out->scales) || out->reserved != 0)
+    return UFP4_ERR_INVALID_ARG;
+  if (axis != UFP4_BLOCKS_ALONG_COLS && axis != UFP4_BLOCKS_ALONG_ROWS) return UFP4_ERR_INVALID_ARG;
+  if (grid != UFP4_GRID_UNIFORM && grid != UFP4_GRID_E2M1) return UFP4_ERR_INVALID_ARG;
+  if (rnd != UFP4_ROUND_RTNE && rnd != UFP4_ROUND_SR) return UFP4_ERR_INVALID_ARG;
+  if (rht != 0 && rht != 1) return UFP4_ERR_INVALID_ARG;
+  if (sign_mask > 0xFFFFu) return UFP4_ERR_INVALID_ARG;
+  if (n_rows <= 0 || n_cols <= 0 || ld < n_cols) return UFP4_ERR_SHAPE;
+  if (axis == UFP4_BLOCKS_ALONG_COLS && (d_group_offsets != nullptr || n_groups != 0))
+    return UFP4_ERR_INVALID_ARG;
+  if (axis == UFP4_BLOCKS_ALONG_ROWS) {
+    if ((d_group_offsets == nullptr) != (n_groups == 0)) return UFP4_ERR_INVALID_ARG;
+    if (d_group_offsets != nullptr && (n_groups < 1 || n_groups > kMaxGroupsApi))
+      return UFP4_ERR_SHAPE;
+  }
+  int64_t rows, kmin;
+  if (axis == UFP4_BLOCKS_ALONG_COLS) {
+    rows = n_rows;
+    kmin = round_up16(n_cols);
+    if (out->kpad != kmin) return UFP4_ERR_SHAPE;
+  } else {
+    rows = n_cols;
+    kmin = d_group_offsets ? round_up16(n_rows + 15 * (int64_t)n_groups) : round_up16(n_rows);
+    if (d_group_offsets ? (out->kpad < kmin || out->kpad % 16 != 0) : (out->kpad != kmin))
+      return UFP4_ERR_SHAPE;
+  }
+  if (out->rows != rows) return UFP4_ERR_SHAPE;
+
+  QuantArgs a{};
+  a.x = x_bf16;
+  a.n_rows = n_rows;
+  a.n_cols = n_cols;
+  a.ld = ld;
+  a.axis = axis;
+  a.goff = d_group_offsets;
+  a.n_groups = n_groups;
+  a.rht = rht;
+  a.sign_mask = sign_mask;
+  a.grid = grid;
+  a.rnd = rnd;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.stream_id = stream_id;
+  a.kpad = out->kpad;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  if (launch_quantize(a, stream) != hipSuccess) return UFP4_ERR_HIP;
+  out->k = (axis == UFP4_BLOCKS_ALONG_COLS) ? n_cols : n_rows;
+  out->grid = grid;
+  out->rht = rht;
+  out->sign_mask = rht ? sign_mask : 0u;
+  return UFP4_OK;
+}
+
+ufp4_status ufp4_dequantize(const ufp4_qtensor *q, int32_t inverse_rht, float *out,
+                            int64_t ld_out, hipStream_t stream) {
+  ufp4_status s = check_qtensor(q);
+  if (s != UFP4_OK) return s;
+  if (out == nullptr || (inverse_rht != 0 && inverse_rht != 1)) return UFP4_ERR_INVALID_ARG;
+  if (inverse_rht && !q->rht) return UFP4_ERR_INVALID_ARG;
+  if (ld_out < q->kpad) return UFP4_ERR_SHAPE;
+  return launch_dequantize(q->codes, q->scales, q->rows, q->kpad, q->grid, inverse_rht != 0,
+                           q->sign_mask, out, ld_out, stream) == hipSuccess
+             ? UFP4_OK
+             : UFP4_ERR_HIP;
+}
+
+ufp4_status ufp4_gemm_fprop(const ufp4_qtensor *xq, const ufp4_qtensor *wq, float *y, int64_t ldy,
+                            hipStream_t stream) {
+  return dense_gemm(xq, wq, y, ldy, stream);
+}
+
+ufp4_status ufp4_gemm_dgrad(const ufp4_qtensor *dyq, const ufp4_qtensor *wtq, float *dx,
+                            int64_t ldx, hipStream_t stream) {
+  return dense_gemm(dyq, wtq, dx, ldx, stream);
+}
+
+ufp4_status ufp4_gemm_wgrad(const ufp4_qtensor *dytq, const ufp4_qtensor *xtq, float *dw,
+                            int64_t lddw, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if ((workspace == nullptr) != (workspace_bytes == 0)) return UFP4_ERR_INVALID_ARG;
+  return dense_gemm(dytq, xtq, dw, lddw, stream);
+}
+
+ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
+                              const ufp4_qtensor *a, const ufp4_qtensor *b, float *c, int64_t ldc,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (kind < 0 || kind > 2) return UFP4_ERR_INVALID_ARG;
+  if (d_group_offsets == nullptr || c == nullptr) return UFP4_ERR_INVALID_ARG;
+  if ((workspace == nullptr) != (workspace_bytes == 0)) return UFP4_ERR_INVALID_ARG;
+  if (n_groups < 1 || n_groups > kMaxGroupsApi) return UFP4_ERR_SHAPE;
+  ufp4_status s = check_pair(a, b);
+  if (s != UFP4_OK) return s;
+  GemmArgs g{};
+  g.a_codes = a->codes;
+  g.a_scales = a->scales;
+  g.b_codes = b->codes;
+  g.b_scales = b->scales;
+  g.kpad = a->kpad;
+  g.c = c;
+  g.ldc = ldc;
+  g.goff = d_group_offsets;
+  g.n_groups = n_groups;
+  g.grid = a->grid;
+  g.M = a->rows;
+  if (kind == 2) {
+    g.mode = 2;
+    g.N = b->rows;
+  } else {
+    g.mode = 1;
+    if (b->rows % n_groups != 0) return UFP4_ERR_SHAPE;
+    g.N = b->rows / n_groups;
+  }
+  if (ldc < g.N) return UFP4_ERR_SHAPE;
+  return launch_gemm(g, stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
+}
+
+size_t ufp4_workspace_size(int32_t kind, int64_t m, int64_t n, int64_t kpad, int32_t n_groups) {
+  (void)kind;
+  (void)m;
+  (void)n;
+  (void)kpad;
+  (void)n_groups;
+  return 0;
+}
+
+const char *ufp4_status_string(ufp4_status status) {
+  switch (status) {
+    case UFP4_OK: return "UFP4_OK";
+    case UFP4_ERR_INVALID_ARG: return "UFP4_ERR_INVALID_ARG";
+    case UFP4_ERR_SHAPE: return "UFP4_ERR_SHAPE";
+    case UFP4_ERR_MISMATCH: return "UFP4_ERR_MISMATCH";
+    case UFP4_ERR_UNSUPPORTED: return "UFP4_ERR_UNSUPPORTED";
+    case UFP4_ERR_HIP: return "UFP4_ERR_HIP";
+  }
+  return "UFP4_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,379 @@
+// Fused RHT + blockwise absmax 4-bit quantizer and the dequantizer (gfx950).
+//
+// Method: "Rethinking Shrinkage Bias in LLM FP4 Pretraining" (arXiv
+// 2606.20381), paperlayer.ai summary, section 2 ("Blockwise quantization",
+// "Rounding rules", "Random Hadamard transforms") and section 4 ("UFP4
+// Recipe").  The pages' fused kernel targets other hardware; this is a
+// memory-bound design for CDNA4: one block of 16 lives in one lane's
+// registers, so the butterfly, absmax and rounding need no cross-lane
+// traffic, and loads/stores are laid out so a wave touches contiguous HBM.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ufp4_device.h"
+#include "ufp4_kernels.h"
+
+namespace ufp4 {
+
+// ---------------------------------------------------------------------------
+// Row-wise: blocks along the contiguous dimension.  One lane per block of 16;
+// consecutive lanes take consecutive blocks of a row, so a wave reads 2 KiB
+// and writes 512 B of codes and 256 B of scales contiguously.
+//   CONTIG: ld == n_cols == kpad (whole input contiguous, no ragged tail).
+//   VEC:    16-byte loads (x 16-byte aligned, ld % 8 == 0), tail guarded.
+// ---------------------------------------------------------------------------
+template <int GRID, int RND, bool RHT, bool CONTIG, bool VEC>
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
+    int64_t kblocks, uint8_t *__restrict__ codes, float *__restrict__ scales,
+    uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id) {
+  const int64_t nblk = n_rows * kblocks;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+    float v[16];
+    if (CONTIG) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(x + b * 16);
+      const uint4 a0 = p[0];
+      const uint4 a1 = p[1];
+      const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = bf16_lo(w[i], RHT ? sign_bit(sign_mask, 2 * i) : 0u);
+        v[2 * i + 1] = bf16_hi(w[i], RHT ? sign_bit(sign_mask, 2 * i + 1) : 0u);
+      }
+    } else {
+      const int64_t row = b / kblocks;
+      const int64_t kb = b - row * kblocks;
+      const int64_t c0 = kb * 16;
+      const uint16_t *p = x + row * ld + c0;
+      if (VEC && c0 + 16 <= n_cols) {
+        const uint4 a0 = *reinterpret_cast<const uint4 *>(p);
+        const uint4 a1 = *reinterpret_cast<const uint4 *>(p + 8);
+        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[2 * i] = bf16_lo(w[i], RHT ? sign_bit(sign_mask, 2 * i) : 0u);
+          v[2 * i + 1] = bf16_hi(w[i], RHT ? sign_bit(sign_mask, 2 * i + 1) : 0u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t h = (c0 + j < n_cols) ? (uint32_t)p[j] : 0u;
+          v[j] = bf16_lo(h, RHT ? sign_bit(sign_mask, j) : 0u);
+        }
+      }
+    }
+    uint32_t w0, w1;
+    float s;
+    quantize_block<GRID, RND, RHT>(v, (uint64_t)b * 16u, seed_lo, seed_hi, stream_id, w0, w1, s);
+    *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(w0, w1);
+    scales[b] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column-wise: blocks along the strided dimension, output transposed.
+// A workgroup owns a tile of 256 padded rows (16 blocks) x 64 columns.  Lane
+// (cp, rq) loads one dword (two adjacent columns) of 16 consecutive rows for
+// row-blocks rq and rq + 8, so every row of the tile is read as 128 contiguous
+// bytes; the four quantized blocks go to LDS and the tile is written back as
+// 64 output rows of 128 contiguous bytes of codes and 64 bytes of scales.
+// Groups: padded block p belongs to the group e with P_e <= 16p < P_{e+1};
+// its rows are off_e + (16p - P_e) + j, zero past the group's end.
+// ---------------------------------------------------------------------------
+constexpr int kColTileRows = 256;
+constexpr int kColTileCols = 64;
+constexpr int kMaxGroups = 1024;
+
+__device__ __forceinline__ int64_t clamp_rows(int64_t v, int64_t n) {
+  return v < 0 ? 0 : (v > n ? n : v);
+}
+
+// Prefix sums of the groups' padded lengths into LDS (block-wide scan).
+__device__ __forceinline__ void load_group_tables(const int64_t *__restrict__ goff,
+                                                  int n_groups, int64_t n_rows,
+                                                  int64_t *s_off, int64_t *s_poff,
+                                                  int64_t *s_scan) {
+  const int tid = threadIdx.x;
+  if (goff == nullptr) {
+    if (tid == 0) {
+      s_off[0] = 0;
+      s_off[1] = n_rows;
+      s_poff[0] = 0;
+      s_poff[1] = (n_rows + 15) / 16 * 16;
+    }
+    __syncthreads();
+    return;
+  }
+  // each thread sums the padded counts of a contiguous run of groups
+  const int per = (n_groups + 255) / 256;
+  const int g0 = tid * per;
+  int64_t local = 0;
+  // offsets are clamped to [0, n_rows] so that no access leaves the input
+  // whatever the device array holds; a decreasing pair is an empty group
+  for (int g = g0; g < g0 + per && g < n_groups; ++g) {
+    const int64_t a = clamp_rows(goff[g], n_rows), b = clamp_rows(goff[g + 1], n_rows);
+    s_off[g] = a;
+    local += (b > a) ? (b - a + 15) / 16 * 16 : 0;
+  }
+  if (tid == 0) s_off[n_groups] = clamp_rows(goff[n_groups], n_rows);
+  s_scan[tid] = local;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 256 partial sums
+  for (int d = 1; d < 256; d <<= 1) {
+    const int64_t add = tid >= d ? s_scan[tid - d] : 0;
+    __syncthreads();
+    s_scan[tid] += add;
+    __syncthreads();
+  }
+  int64_t run = tid ? s_scan[tid - 1] : 0;
+  for (int g = g0; g < g0 + per && g < n_groups; ++g) {
+    s_poff[g] = run;
+    const int64_t cnt = s_off[g + 1] - s_off[g];
+    run += (cnt > 0) ? (cnt + 15) / 16 * 16 : 0;
+  }
+  if (tid == 255) s_poff[n_groups] = s_scan[255];
+  __syncthreads();
+}
+
+// Largest e with s_poff[e] <= p16 (s_poff non-decreasing, s_poff[0] = 0).
+__device__ __forceinline__ int find_group(const int64_t *s_poff, int n_groups, int64_t p16) {
+  int lo = 0, hi = n_groups;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_poff[mid] <= p16) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <int GRID, int RND, bool RHT, bool VEC>
+__global__ __launch_bounds__(256) void quant_cols_kernel(
+    const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
+    const int64_t *__restrict__ goff, int n_groups, int64_t kpad, uint8_t *__restrict__ codes,
+    float *__restrict__ scales, uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi,
+    uint32_t stream_id) {
+  __shared__ int64_t s_off[kMaxGroups + 1];
+  __shared__ int64_t s_poff[kMaxGroups + 1];
+  __shared__ int64_t s_scan[256];
+  __shared__ uint2 s_codes[kColTileCols][kColTileRows / 16 + 1];
+  __shared__ float s_scales[kColTileCols][kColTileRows / 16 + 1];
+
+  const int ng = goff ? n_groups : 1;
+  load_group_tables(goff, n_groups, n_rows, s_off, s_poff, s_scan);
+
+  const int tid = threadIdx.x;
+  const int cp = tid & 31;   // column pair within the tile
+  const int rq = tid >> 5;   // 0..7
+  const int64_t kblocks = kpad / 16;
+  const int64_t n_ptiles = (kpad + kColTileRows - 1) / kColTileRows;
+  const int64_t n_ctiles = (n_cols + kColTileCols - 1) / kColTileCols;
+  const int64_t total = n_ptiles * n_ctiles;
+  const int64_t padded_end = s_poff[ng];
+
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int64_t pt = tile % n_ptiles;
+    const int64_t ct = tile / n_ptiles;
+    const int64_t pb0 = pt * (kColTileRows / 16);   // first padded block of the tile
+    const int64_t col0 = ct * kColTileCols;
+    const int64_t col = col0 + 2 * cp;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int rb = rq + 8 * half;                   // block within the tile
+      const int64_t p = pb0 + rb;                     // padded block index
+      float va[16], vb[16];
+      int64_t row0 = 0;
+      int valid = 0;
+      if (p < kblocks && 16 * p < padded_end) {
+        const int e = find_group(s_poff, ng, 16 * p);
+        row0 = s_off[e] + (16 * p - s_poff[e]);
+        const int64_t left = s_off[e + 1] - row0;
+        valid = left >= 16 ? 16 : (int)(left > 0 ? left : 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        uint32_t w = 0u;
+        if (j < valid) {
+          const uint16_t *q = x + (row0 + j) * ld + col;
+          if (VEC && col + 1 < n_cols) {
+            w = *reinterpret_cast<const uint32_t *>(q);
+          } else {
+            const uint32_t a = col < n_cols ? (uint32_t)q[0] : 0u;
+            const uint32_t b = col + 1 < n_cols ? (uint32_t)q[1] : 0u;
+            w = a | (b << 16);
+          }
+        }
+        va[j] = bf16_lo(w, RHT ? sign_bit(sign_mask, j) : 0u);
+        vb[j] = bf16_hi(w, RHT ? sign_bit(sign_mask, j) : 0u);
+      }
+      uint32_t a0, a1, b0, b1;
+      float sa, sb;
+      const uint64_t base_a = (uint64_t)col * (uint64_t)kpad + (uint64_t)p * 16u;
+      const uint64_t base_b = base_a + (uint64_t)kpad;
+      quantize_block<GRID, RND, RHT>(va, base_a, seed_lo, seed_hi, stream_id, a0, a1, sa);
+      quantize_block<GRID, RND, RHT>(vb, base_b, seed_lo, seed_hi, stream_id, b0, b1, sb);
+      s_codes[2 * cp][rb] = make_uint2(a0, a1);
+      s_codes[2 * cp + 1][rb] = make_uint2(b0, b1);
+      s_scales[2 * cp][rb] = sa;
+      s_scales[2 * cp + 1][rb] = sb;
+    }
+    __syncthreads();
+    // write back: 64 columns x 16 blocks of 8-byte codes, lane -> (column, block)
+    const int nb = (int)((kblocks - pb0) < 16 ? (kblocks - pb0) : 16);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + 256 * it;      // 0..1023
+      const int c = i >> 4;
+      const int blk = i & 15;
+      const int64_t oc = col0 + c;
+      if (oc < n_cols && blk < nb) {
+        uint2 *dst = reinterpret_cast<uint2 *>(codes + oc * (kpad / 2) + (pb0 + blk) * 8);
+        *dst = s_codes[c][blk];
+        scales[oc * kblocks + pb0 + blk] = s_scales[c][blk];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantizer: one lane per block.  value = (float)((double)(sign*L) *
+// (double)s / g); with the inverse RHT the FP64 block goes back through
+// (1/4) D H16 (same butterfly order) before the cast.
+// ---------------------------------------------------------------------------
+template <int GRID, bool INV>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
+                                                      const float *__restrict__ scales,
+                                                      int64_t rows, int64_t kblocks,
+                                                      float *__restrict__ out, int64_t ld_out,
+                                                      uint32_t sign_mask) {
+  const int64_t nblk = rows * kblocks;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+    const int64_t row = b / kblocks;
+    const int64_t kb = b - row * kblocks;
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + b * 8);
+    const double s = (double)scales[b];
+    constexpr double g = (GRID == kGridUniform) ? 7.0 : 6.0;
+    double d[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t w = j < 8 ? c.x : c.y;
+      const uint32_t n = (w >> (4 * (j & 7))) & 0xFu;
+      const uint32_t mi = n & 7u;
+      double lv;
+      if (GRID == kGridUniform) {
+        lv = (double)mi;
+      } else {
+        lv = mi < 4 ? 0.5 * (double)mi : (mi == 4 ? 2.0 : (mi == 5 ? 3.0 : (mi == 6 ? 4.0 : 6.0)));
+      }
+      if (n & 8u) lv = -lv;
+      d[j] = lv * s / g;
+    }
+    if (INV) {
+#pragma unroll
+      for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if ((i & h) == 0) {
+            const double a = d[i], bb = d[i + h];
+            d[i] = a + bb;
+            d[i + h] = a - bb;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        d[j] *= 0.25;
+        if ((sign_mask >> j) & 1u) d[j] = -d[j];
+      }
+    }
+    float *o = out + row * ld_out + kb * 16;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[j] = (float)d[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (host side).  Grids are sized to a few waves of workgroups per CU
+// and the kernels grid-stride, so any size runs with bounded launches.
+// ---------------------------------------------------------------------------
+static int grid_for(int64_t work_items, int per_block, int max_blocks) {
+  int64_t b = (work_items + per_block - 1) / per_block;
+  if (b > max_blocks) b = max_blocks;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+template <int GRID, int RND, bool RHT>
+static hipError_t launch_rows_t(const QuantArgs &a, hipStream_t st) {
+  const int64_t kblocks = a.kpad / 16;
+  const int64_t nblk = a.n_rows * kblocks;
+  const int blocks = grid_for(nblk, 256, 256 * 16);
+  const bool contig = (a.ld == a.n_cols) && (a.n_cols % 16 == 0) &&
+                      ((reinterpret_cast<uintptr_t>(a.x) & 15u) == 0);
+  const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 15u) == 0) && (a.ld % 8 == 0);
+  if (contig)
+    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, true, true>), dim3(blocks), dim3(256), 0,
+                       st, a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
+                       a.seed_lo, a.seed_hi, a.stream_id);
+  else if (vec)
+    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, false, true>), dim3(blocks), dim3(256), 0,
+                       st, a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
+                       a.seed_lo, a.seed_hi, a.stream_id);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, false, false>), dim3(blocks), dim3(256), 0,
+                       st, a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
+                       a.seed_lo, a.seed_hi, a.stream_id);
+  return hipGetLastError();
+}
+
+template <int GRID, int RND, bool RHT>
+static hipError_t launch_cols_t(const QuantArgs &a, hipStream_t st) {
+  const int64_t n_ptiles = (a.kpad + kColTileRows - 1) / kColTileRows;
+  const int64_t n_ctiles = (a.n_cols + kColTileCols - 1) / kColTileCols;
+  const int blocks = grid_for(n_ptiles * n_ctiles, 1, 256 * 8);
+  const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0);
+  if (vec)
+    hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, true>), dim3(blocks), dim3(256), 0, st,
+                       a.x, a.n_rows, a.n_cols, a.ld, a.goff, a.n_groups, a.kpad, a.codes,
+                       a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id);
+  else
+    hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, false>), dim3(blocks), dim3(256), 0, st,
+                       a.x, a.n_rows, a.n_cols, a.ld, a.goff, a.n_groups, a.kpad, a.codes,
+                       a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id);
+  return hipGetLastError();
+}
+
+template <int GRID, int RND>
+static hipError_t launch_q2(const QuantArgs &a, hipStream_t st) {
+  if (a.axis == 0)
+    return a.rht ? launch_rows_t<GRID, RND, true>(a, st) : launch_rows_t<GRID, RND, false>(a, st);
+  return a.rht ? launch_cols_t<GRID, RND, true>(a, st) : launch_cols_t<GRID, RND, false>(a, st);
+}
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t st) {
+  if (a.grid == kGridUniform)
+    return a.rnd == kRoundSR ? launch_q2<kGridUniform, kRoundSR>(a, st)
+                             : launch_q2<kGridUniform, kRoundRTNE>(a, st);
+  return a.rnd == kRoundSR ? launch_q2<kGridE2M1, kRoundSR>(a, st)
+                           : launch_q2<kGridE2M1, kRoundRTNE>(a, st);
+}
+
+hipError_t launch_dequantize(const uint8_t *codes, const float *scales, int64_t rows,
+                             int64_t kpad, int grid, bool inverse, uint32_t sign_mask, float *out,
+                             int64_t ld_out, hipStream_t st) {
+  const int64_t kblocks = kpad / 16;
+  const int blocks = grid_for(rows * kblocks, 256, 256 * 16);
+#define UFP4_DQ(G, I)                                                                      \
+  hipLaunchKernelGGL((dequant_kernel<G, I>), dim3(blocks), dim3(256), 0, st, codes, scales, \
+                     rows, kblocks, out, ld_out, sign_mask)
+  if (grid == kGridUniform) {
+    if (inverse) UFP4_DQ(kGridUniform, true); else UFP4_DQ(kGridUniform, false);
+  } else {
+    if (inverse) UFP4_DQ(kGridE2M1, true); else UFP4_DQ(kGridE2M1, false);
+  }
+#undef UFP4_DQ
+  return hipGetLastError();
+}
+
+}  // namespace ufp4

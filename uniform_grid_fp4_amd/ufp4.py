@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libufp4.so.
+
+Argument marshalling only: torch provides device memory (every output is a
+torch tensor allocated here and handed to the library as a raw pointer) and
+the current stream; every step of the computation runs in the library's HIP
+kernels.  The binding fails loudly if the library is missing -- there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libufp4.so")
+
+GRID_UNIFORM, GRID_E2M1 = 0, 1
+ROUND_RTNE, ROUND_SR = 0, 1
+BLOCKS_ALONG_COLS, BLOCKS_ALONG_ROWS = 0, 1
+FPROP, DGRAD, WGRAD = 0, 1, 2
+
+STATUS = {0: "UFP4_OK", -1: "UFP4_ERR_INVALID_ARG", -2: "UFP4_ERR_SHAPE",
+          -3: "UFP4_ERR_MISMATCH", -4: "UFP4_ERR_UNSUPPORTED", -5: "UFP4_ERR_HIP"}
+
+# Every symbol include/ufp4.h declares.
+EXPORTS = ("ufp4_rht_quantize", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
+           "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_workspace_size",
+           "ufp4_status_string")
+
+
+class UFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class QTensorDesc(ctypes.Structure):
+    """Mirror of ufp4_qtensor."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("k", ctypes.c_int64), ("kpad", ctypes.c_int64),
+                ("grid", ctypes.c_int32), ("rht", ctypes.c_int32),
+                ("sign_mask", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libufp4.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m uniform_grid_fp4_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I64, I32, U32, U64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
+    Q = ctypes.POINTER(QTensorDesc)
+    L.ufp4_rht_quantize.argtypes = [P, I64, I64, I64, I32, P, I32, I32, U32, I32, I32, U64, U32,
+                                    Q, P]
+    L.ufp4_dequantize.argtypes = [Q, I32, P, I64, P]
+    L.ufp4_gemm_fprop.argtypes = [Q, Q, P, I64, P]
+    L.ufp4_gemm_dgrad.argtypes = [Q, Q, P, I64, P]
+    L.ufp4_gemm_wgrad.argtypes = [Q, Q, P, I64, P, ctypes.c_size_t, P]
+    L.ufp4_grouped_gemm.argtypes = [I32, I32, P, Q, Q, P, I64, P, ctypes.c_size_t, P]
+    L.ufp4_workspace_size.argtypes = [I32, I64, I64, I64, I32]
+    L.ufp4_workspace_size.restype = ctypes.c_size_t
+    L.ufp4_status_string.argtypes = [I32]
+    L.ufp4_status_string.restype = ctypes.c_char_p
+    for f in ("ufp4_rht_quantize", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
+              "ufp4_gemm_wgrad", "ufp4_grouped_gemm"):
+        getattr(L, f).restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise UFP4Error(status, where)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+@dataclass
+class Quantized:
+    """A quantized operand: codes [rows, kpad/2] uint8 and scales [rows,
+    kpad/16] float32 on the GPU, plus what the GEMMs need to check."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    k: int
+    kpad: int
+    grid: int
+    rht: int
+    sign_mask: int
+
+    def desc(self) -> QTensorDesc:
+        return QTensorDesc(self.codes.data_ptr(), self.scales.data_ptr(), self.rows, self.k,
+                           self.kpad, self.grid, self.rht, self.sign_mask, 0)
+
+
+def padded_k_capacity(n_rows: int, n_groups: int) -> int:
+    """Smallest kpad a grouped ALONG_ROWS quantization accepts."""
+    return (n_rows + 15 * n_groups + 15) // 16 * 16
+
+
+def ufp4_rht_quantize(x: torch.Tensor, axis: int = BLOCKS_ALONG_COLS, rht: bool = True,
+                      sign_mask: int = 0, grid: int = GRID_UNIFORM, rnd: int = ROUND_RTNE,
+                      seed: int = 0, stream_id: int = 0,
+                      group_offsets: Optional[torch.Tensor] = None,
+                      kpad: Optional[int] = None) -> Quantized:
+    """Quantize a 2-D bf16 CUDA tensor (any row stride, unit column stride)."""
+    assert x.dim() == 2 and x.dtype == torch.bfloat16 and x.is_cuda and x.stride(1) == 1
+    n_rows, n_cols = x.shape
+    n_groups = 0
+    if axis == BLOCKS_ALONG_COLS:
+        rows, kp = n_rows, (n_cols + 15) // 16 * 16
+    else:
+        rows = n_cols
+        if group_offsets is not None:
+            assert group_offsets.dtype == torch.int64 and group_offsets.is_cuda
+            n_groups = group_offsets.numel() - 1
+            kp = kpad if kpad is not None else padded_k_capacity(n_rows, n_groups)
+        else:
+            kp = (n_rows + 15) // 16 * 16
+    codes = torch.empty((rows, kp // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, kp // 16), dtype=torch.float32, device=x.device)
+    d = QTensorDesc(codes.data_ptr(), scales.data_ptr(), rows, 0, kp, 0, 0, 0, 0)
+    st = lib().ufp4_rht_quantize(_ptr(x), n_rows, n_cols, x.stride(0), axis,
+                                 _ptr(group_offsets), n_groups, int(rht), sign_mask, grid, rnd,
+                                 seed, stream_id, ctypes.byref(d), _stream(x.device))
+    _check(st, "ufp4_rht_quantize")
+    return Quantized(codes, scales, rows, d.k, kp, d.grid, d.rht, d.sign_mask)
+
+
+def ufp4_dequantize(q: Quantized, inverse_rht: bool = False) -> torch.Tensor:
+    out = torch.empty((q.rows, q.kpad), dtype=torch.float32, device=q.codes.device)
+    d = q.desc()
+    st = lib().ufp4_dequantize(ctypes.byref(d), int(inverse_rht), _ptr(out), q.kpad,
+                               _stream(out.device))
+    _check(st, "ufp4_dequantize")
+    return out
+
+
+def _dense(fn, name, a: Quantized, b: Quantized, out: Optional[torch.Tensor], *extra):
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=torch.float32, device=a.codes.device)
+    da, db = a.desc(), b.desc()
+    st = fn(ctypes.byref(da), ctypes.byref(db), _ptr(out), out.stride(0), *extra,
+            _stream(out.device))
+    _check(st, name)
+    return out
+
+
+def ufp4_gemm_fprop(xq: Quantized, wq: Quantized, out: Optional[torch.Tensor] = None):
+    """Y = X_hat W_hat^T, [T, F] FP32."""
+    return _dense(lib().ufp4_gemm_fprop, "ufp4_gemm_fprop", xq, wq, out)
+
+
+def ufp4_gemm_dgrad(dyq: Quantized, wtq: Quantized, out: Optional[torch.Tensor] = None):
+    """dX = dY_hat (W^T)_hat^T, [T, H] FP32."""
+    return _dense(lib().ufp4_gemm_dgrad, "ufp4_gemm_dgrad", dyq, wtq, out)
+
+
+def ufp4_gemm_wgrad(dytq: Quantized, xtq: Quantized, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """dW = (dY^T)_hat (X^T)_hat^T, [F, H] FP32."""
+    ws = _ptr(workspace)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return _dense(lib().ufp4_gemm_wgrad, "ufp4_gemm_wgrad", dytq, xtq, out, ws, nbytes)
+
+
+def ufp4_grouped_gemm(kind: int, group_offsets: torch.Tensor, a: Quantized, b: Quantized,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """Expert-grouped GEMM; see include/ufp4.h for the three kinds."""
+    n_groups = group_offsets.numel() - 1
+    if kind == WGRAD:
+        shape = (n_groups, a.rows, b.rows)
+        ldc = b.rows
+    else:
+        n = b.rows // n_groups
+        shape = (a.rows, n)
+        ldc = n
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=a.codes.device)
+    da, db = a.desc(), b.desc()
+    ws = _ptr(workspace)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().ufp4_grouped_gemm(kind, n_groups, _ptr(group_offsets), ctypes.byref(da),
+                                 ctypes.byref(db), _ptr(out), ldc, ws, nbytes,
+                                 _stream(out.device))
+    _check(st, "ufp4_grouped_gemm")
+    return out
+
+
+def ufp4_workspace_size(kind: int, m: int, n: int, kpad: int, n_groups: int = 1) -> int:
+    return int(lib().ufp4_workspace_size(kind, m, n, kpad, n_groups))
+
+
+def ufp4_status_string(status: int) -> str:
+    return lib().ufp4_status_string(status).decode()
