@@ -1,0 +1,240 @@
+"""Throughput of the UFP4 hot path on one MI355X.
+
+A step is one pass of the whole path over the dense 1.5B-model linear layer
+(tokens 8192, hidden 2048, FFN 8192): the six quantizations of the UFP4
+recipe (X and W along H for FPROP; dY along F with stochastic rounding and W
+along F for DGRAD; dY and X along the tokens for WGRAD, dY with stochastic
+rounding) and the three block-scaled 4-bit GEMMs.  Inputs are synthetic
+(seeded, see uniform_grid_fp4_amd/workloads.py) and resident in HBM before
+the timed region.
+
+Prints one JSON line.  `value` is the whole step's throughput in GEMM
+TFLOP/s (3 x 2*T*H*F FLOP per step over the wall time of the step, the six
+quantizations included); the quantizer and GEMM kernels are also reported on
+their own, timed with HIP events on the stream they run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA
+# The GEMM is bound by its per-block FP32 rescale on the vector ALU: two VALU
+# operations (a multiply and an FMA) per output per 16-element block, i.e.
+# 2 ops per 16 MACs.  Non-packed FP32 VALU issue: 256 CU x 4 SIMD x 16 lanes
+# x 2.4 GHz = 39.32e12 lane-ops/s, so the GEMM ceiling is
+# 39.32e12 * 16 MAC / 2 ops * 2 FLOP/MAC = 629.1 TFLOP/s.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+GEMM_ALU_PEAK_TFLOPS = VALU_LANE_OPS * 16.0 / 2.0 * 2.0 / 1e12
+BYTES_PER_QUANT_ELEM = 2.0 + 0.5 + 0.25
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+class Step:
+    """Buffers and calls of one pass of the hot path."""
+
+    def __init__(self, L, U, torch):
+        self.L, self.U, self.torch = L, U, torch
+        T, H, F = L.x.shape[0], L.hidden, L.ffn
+        self.T, self.H, self.F = T, H, F
+        self.mf, self.md, self.mw = L.masks
+        dev = L.x.device
+        self.y = torch.empty((T, F), dtype=torch.float32, device=dev)
+        self.dx = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.dw = torch.empty((F, H), dtype=torch.float32, device=dev)
+        self.q = {}
+        self.seed = 1234
+        self.run(None)   # allocates the quantized buffers once
+
+    def quant(self, name, x, axis, mask, rnd, sid, ev):
+        U = self.U
+        if ev is not None:
+            ev[name][0].record()
+        q = U.ufp4_rht_quantize(x, axis, True, mask, U.GRID_UNIFORM, rnd, self.seed, sid,
+                                out=self.q.get(name))
+        if ev is not None:
+            ev[name][1].record()
+        self.q[name] = q
+        return q
+
+    def gemm(self, name, fn, a, b, out, ev):
+        if ev is not None:
+            ev[name][0].record()
+        fn(a, b, out=out)
+        if ev is not None:
+            ev[name][1].record()
+
+    def run(self, ev):
+        U, L = self.U, self.L
+        C, R = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS
+        xq = self.quant("q_x_fprop", L.x, C, self.mf, U.ROUND_RTNE, 0, ev)
+        wq = self.quant("q_w_fprop", L.w, C, self.mf, U.ROUND_RTNE, 0, ev)
+        self.gemm("fprop", U.ufp4_gemm_fprop, xq, wq, self.y, ev)
+        dyq = self.quant("q_dy_dgrad", L.dy, C, self.md, U.ROUND_SR, 0, ev)
+        wtq = self.quant("q_wt_dgrad", L.w, R, self.md, U.ROUND_RTNE, 0, ev)
+        self.gemm("dgrad", U.ufp4_gemm_dgrad, dyq, wtq, self.dx, ev)
+        dytq = self.quant("q_dyt_wgrad", L.dy, R, self.mw, U.ROUND_SR, 1, ev)
+        xtq = self.quant("q_xt_wgrad", L.x, R, self.mw, U.ROUND_RTNE, 0, ev)
+        self.gemm("wgrad", U.ufp4_gemm_wgrad, dytq, xtq, self.dw, ev)
+
+    QUANT = ("q_x_fprop", "q_w_fprop", "q_dy_dgrad", "q_wt_dgrad", "q_dyt_wgrad", "q_xt_wgrad")
+    GEMMS = ("fprop", "dgrad", "wgrad")
+
+    def quant_elems(self):
+        T, H, F = self.T, self.H, self.F
+        return {"q_x_fprop": T * H, "q_w_fprop": F * H, "q_dy_dgrad": T * F,
+                "q_wt_dgrad": F * H, "q_dyt_wgrad": T * F, "q_xt_wgrad": T * H}
+
+    def gemm_flops(self):
+        return 2.0 * self.T * self.H * self.F
+
+
+def cpu_baseline(L, target_s: float):
+    """The oracle on the host, on a bounded sample of the same workload: it
+    quantizes a sample of rows of each operand and runs the FP64 GEMM on a
+    sample of output rows; the per-element and per-FLOP rates are scaled to a
+    whole step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import ufp4_oracle as O
+    from uniform_grid_fp4_amd import workloads as W
+
+    xb, wb, dyb = W.bits_numpy(L.x), W.bits_numpy(L.w), W.bits_numpy(L.dy)
+    mf, md, mw = L.masks
+    T, H, F = xb.shape[0], L.hidden, L.ffn
+    # quantizer rate: rows of X and dY, row-wise and column-wise, RTNE and SR
+    t0 = time.perf_counter()
+    n_el = 0
+    rows = np.arange(64)
+    for bits, axis, rnd in ((xb, 0, 0), (dyb, 0, 1), (xb, 1, 0), (dyb, 1, 1)):
+        c, s, kp = O.quantize(bits, axis, True, mf, O.GRID_UNIFORM, rnd, 1234, 0, out_rows=rows)
+        n_el += c.shape[0] * kp
+        if time.perf_counter() - t0 > target_s / 2:
+            break
+    tq = time.perf_counter() - t0
+    q_rate = n_el / tq
+    # GEMM rate: FPROP on sampled output rows (B = the whole quantized W)
+    cw, sw, _ = O.quantize(wb, 0, True, mf, O.GRID_UNIFORM, 0)
+    cx, sx, _ = O.quantize(xb, 0, True, mf, O.GRID_UNIFORM, 0, out_rows=np.arange(256))
+    t1 = time.perf_counter()
+    flops = 0.0
+    done = 0
+    while True:
+        r0 = done % 256
+        Cr, _ = O.gemm_tn_rows(cx, sx, cw, sw, np.arange(r0, r0 + 32))
+        flops += 2.0 * 32 * F * H
+        done += 32
+        if time.perf_counter() - t1 > target_s / 2:
+            break
+    tg = time.perf_counter() - t1
+    g_rate = flops / tg
+    elems_step = 2 * (T * H + F * H + T * F)
+    step_s = elems_step / q_rate + 3 * 2.0 * T * H * F / g_rate
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": 3 * 2.0 * T * H * F / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"oracle quantizer on {n_el} elements (64-row samples of X and dY, row- and "
+                   f"column-wise, RTNE and SR: {q_rate / 1e6:.2f} M elem/s) and FP64 FPROP on "
+                   f"{done} output rows ({g_rate / 1e9:.1f} GFLOP/s), scaled to one step "
+                   f"({step_s:.1f} s); host cpu_count={os.cpu_count()}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the UFP4 hot path is "
+              "data parallel and this build measures one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from uniform_grid_fp4_amd import ufp4 as U
+    from uniform_grid_fp4_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    L = W.dense_1p5b(dev)
+    st = Step(L, U, torch)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        st.run(None)
+    torch.cuda.synchronize()
+
+    names = Step.QUANT + Step.GEMMS
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in names} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        st.run(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    dur = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}
+    qel = st.quant_elems()
+    q_ms = sum(dur[n] for n in Step.QUANT)
+    q_bytes = sum(qel.values()) * BYTES_PER_QUANT_ELEM
+    g_ms = sum(dur[n] for n in Step.GEMMS)
+    g_flop = 3 * st.gemm_flops()
+    gemm_avg_ms = g_ms / 3
+    gemm_tflops = st.gemm_flops() / (gemm_avg_ms * 1e-3) / 1e12
+    step_tflops = g_flop / (ms_step * 1e-3) / 1e12
+
+    out = {
+        "metric": "RHT+UFP4 quantize GB/s (% HBM peak); UFP4 GEMM TFLOP/s (% MFMA peak)",
+        "value": round(step_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 MFMA operands (exact 4-bit levels), fp32 accumulate/scales",
+        "data": "synthetic",
+        "config": {"workload": L.name, "tokens": st.T, "hidden": st.H, "ffn": st.F,
+                   "recipe": "UFP4: uniform grid, RHT-16 on all 3 GEMMs, SR on dY",
+                   "block": 16, "scale": "fp32 absmax"},
+        "quantize": {"gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "ms_per_step": round(q_ms, 4),
+                     "per_call_ms": {n: round(dur[n], 4) for n in Step.QUANT},
+                     "bytes_per_step": q_bytes},
+        "gemm": {"tflops": round(gemm_tflops, 2),
+                 "frac_fp8_mfma_peak": round(gemm_tflops / FP8_MFMA_PEAK_TFLOPS, 4),
+                 "ms_per_step": round(g_ms, 4),
+                 "per_call_ms": {n: round(dur[n], 4) for n in Step.GEMMS}},
+        "roofline": {"kernel": "ufp4::gemm_kernel<0>", "bound": "alu",
+                     "achieved": round(gemm_tflops, 2), "peak": round(GEMM_ALU_PEAK_TFLOPS, 1),
+                     "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / GEMM_ALU_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,15 +11,20 @@
 // Design for gfx950: every grid level is an exact FP8 E4M3 value (uniform:
 // 0..7; E2M1 doubled: 0,1,2,3,4,6,8,12), so one v_mfma_f32_32x32x16_fp8_fp8
 // per 16-element block yields P_kb exactly in FP32 (|P| <= 16*144).  The
-// per-block rescale is an FP32 multiply and fused multiply-add per output on
-// the vector ALU, which is the bound of this kernel (two VALU operations per
-// 16 MACs); the MFMA of the next tile overlaps it.  Nibbles are expanded to
-// FP8 once per workgroup while staging into LDS (v_perm_b32 look-up), so the
-// waves only read ready operands.
+// per-block rescale is an FP32 multiply and an FMA per output on the vector
+// ALU -- two VALU operations per 16 MACs -- and that, not the matrix core,
+// bounds this kernel; MFMAs of one wave overlap the rescale of the other wave
+// on the same SIMD.  Nibbles are expanded to FP8 (v_perm_b32 look-up) once per
+// workgroup while staging into LDS, so the waves read ready MFMA operands.
 //
-// Tiling: 256 threads = 4 waves, 128 x 128 output tile, each wave 32 rows x
-// 128 columns = four 32x32 MFMA tiles sharing one A fragment and one set of
-// 16 row scales per block.  K advances 64 (4 blocks) per LDS stage.
+// Tiling: 512 threads = 8 waves, 256 x 128 output tile; wave w owns rows
+// [32w, 32w+32) x 128 columns = four 32x32 MFMA tiles sharing one A fragment
+// and one set of 16 row scales per block.  K advances 128 (8 blocks) per LDS
+// stage, double-buffered: the global loads of stage s+1 are in flight while
+// stage s is computed, and there is one barrier per stage.  Operands are read
+// with buffer loads whose range check returns zero past the tile's rows, so
+// ragged edges need no branches.  Tiles are assigned XCD-major: the 8 XCDs
+// each walk a contiguous range of tiles, so a row panel of A stays in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,14 +35,25 @@ namespace ufp4 {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;
+constexpr int kThreads = 512;
+constexpr int kBM = 256;
 constexpr int kBN = 128;
-constexpr int kStageBlocks = 4;                 // 16-element blocks per stage
-constexpr int kRowBytes = kStageBlocks * 16 + 8; // fp8 bytes per LDS row (+8 pad)
+constexpr int kSB = 8;                        // 16-element blocks per stage
+constexpr int kRowBytes = kSB * 16 + 8;       // FP8 bytes per LDS row (+8 breaks bank aliasing)
+constexpr int kAItems = kBM * kSB / kThreads; // (row, block) items per thread: 4
+constexpr int kBItems = kBN * kSB / kThreads; // 2
 constexpr int kMaxGemmGroups = 1024;
+constexpr int kXcds = 8;
+
+struct Stage {
+  uint8_t a[kBM * kRowBytes];
+  uint8_t b[kBN * kRowBytes];
+  float sa[kSB * kBM];   // block-major: sa[blk][row]
+  float sb[kSB * kBN];
+};
 
 // 8 nibbles -> 8 FP8 E4M3 bytes.  Output byte order [n0 n2 n4 n6 | n1 n3 n5
-// n7]; A and B use the same order so products still pair up.
+// n7]; A and B use the same order, so products still pair up.
 template <int GRID>
 __device__ __forceinline__ uint2 nib8_to_fp8(uint32_t w) {
   constexpr uint32_t lut_lo = 0x44403800u;  // 0, 1, 2, 3
@@ -51,79 +67,116 @@ __device__ __forceinline__ uint2 nib8_to_fp8(uint32_t w) {
 }
 
 struct TileJob {
-  int64_t a_row0, a_row_end;   // A rows of this tile [a_row0, a_row_end)
-  int64_t b_row0, b_row_end;   // B rows
-  int64_t kb0, kb1;            // block range [kb0, kb1)
-  float *c;                    // C element (0,0) of the tile
-  int64_t ldc;
+  int64_t a_row0, a_rows;   // A rows [a_row0, a_row0 + a_rows)
+  int64_t b_row0, b_rows;
+  int64_t kb0, kb1;         // block range [kb0, kb1)
+  float *c;                 // C element (0, 0) of the tile
 };
 
-// Stage one K slice of the A or B tile: 128 rows x 4 blocks.  Thread t takes
-// (row, block) items t and t + 256.
-template <int GRID>
-__device__ __forceinline__ void stage_operand(const uint8_t *__restrict__ codes,
-                                              const float *__restrict__ scales, int64_t kpad,
-                                              int64_t row0, int64_t row_end, int64_t kb,
-                                              int64_t kb_end, uint8_t *s_q, float *s_s) {
-  const int64_t kblocks = kpad / 16;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int i = threadIdx.x + 256 * it;
-    const int r = i >> 2;
-    const int b = i & 3;
-    const int64_t row = row0 + r;
-    const int64_t blk = kb + b;
-    uint2 w = make_uint2(0u, 0u);
-    float s = 0.0f;
-    if (row < row_end && blk < kb_end) {
-      w = *reinterpret_cast<const uint2 *>(codes + row * (kpad / 2) + blk * 8);
-      s = scales[row * kblocks + blk];
-    }
-    const uint2 lo = nib8_to_fp8<GRID>(w.x);
-    const uint2 hi = nib8_to_fp8<GRID>(w.y);
-    uint2 *dst = reinterpret_cast<uint2 *>(s_q + r * kRowBytes + b * 16);
-    dst[0] = lo;
-    dst[1] = hi;
-    s_s[b * kBM + r] = s;
-  }
+// Per-thread staging registers of one stage.
+struct Regs {
+  uint2 aq[kAItems];
+  float as[kAItems];
+  uint2 bq[kBItems];
+  float bs[kBItems];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
 template <int GRID>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileJob &job, uint8_t *s_a,
-                                          uint8_t *s_b, float *s_sa, float *s_sb) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int l32 = lane & 31;
-  const int half = lane >> 5;
-  floatx16 acc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
-  const floatx16 zero = acc[0];
+struct Gemm {
+  const GemmArgs &g;
+  TileJob job;
+  __amdgpu_buffer_rsrc_t ra_q, ra_s, rb_q, rb_s;
+  int64_t kblocks;
 
-  for (int64_t kb = job.kb0; kb < job.kb1; kb += kStageBlocks) {
-    stage_operand<GRID>(g.a_codes, g.a_scales, g.kpad, job.a_row0, job.a_row_end, kb, job.kb1,
-                        s_a, s_sa);
-    stage_operand<GRID>(g.b_codes, g.b_scales, g.kpad, job.b_row0, job.b_row_end, kb, job.kb1,
-                        s_b, s_sb);
-    __syncthreads();
+  __device__ Gemm(const GemmArgs &args, const TileJob &j) : g(args), job(j) {
+    kblocks = g.kpad / 16;
+    // Resources start at the tile's first row, so 32-bit offsets suffice and
+    // rows past the tile read as zero.
+    ra_q = make_rsrc(g.a_codes + job.a_row0 * (g.kpad / 2), job.a_rows * (g.kpad / 2));
+    ra_s = make_rsrc(g.a_scales + job.a_row0 * kblocks, job.a_rows * kblocks * 4);
+    rb_q = make_rsrc(g.b_codes + job.b_row0 * (g.kpad / 2), job.b_rows * (g.kpad / 2));
+    rb_s = make_rsrc(g.b_scales + job.b_row0 * kblocks, job.b_rows * kblocks * 4);
+  }
+
+  __device__ __forceinline__ void load(Regs &r, int64_t kb) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kAItems; ++j) {
+      const int i = tid + kThreads * j;
+      const int row = i >> 3, blk = i & 7;
+      const bool ok = kb + blk < job.kb1;
+      const int oq = ok ? (int)(row * (g.kpad / 2) + (kb + blk) * 8) : 0x7FFFFFF8;
+      const int os = ok ? (int)((row * kblocks + kb + blk) * 4) : 0x7FFFFFF8;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra_q, oq, 0, 0);
+      r.aq[j] = make_uint2(v[0], v[1]);
+      r.as[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra_s, os, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kBItems; ++j) {
+      const int i = tid + kThreads * j;
+      const int row = i >> 3, blk = i & 7;
+      const bool ok = kb + blk < job.kb1;
+      const int oq = ok ? (int)(row * (g.kpad / 2) + (kb + blk) * 8) : 0x7FFFFFF8;
+      const int os = ok ? (int)((row * kblocks + kb + blk) * 4) : 0x7FFFFFF8;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rb_q, oq, 0, 0);
+      r.bq[j] = make_uint2(v[0], v[1]);
+      r.bs[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_s, os, 0, 0));
+    }
+  }
+
+  __device__ __forceinline__ static void store(const Regs &r, Stage &s) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kAItems; ++j) {
+      const int i = tid + kThreads * j;
+      const int row = i >> 3, blk = i & 7;
+      uint2 *dst = reinterpret_cast<uint2 *>(s.a + row * kRowBytes + blk * 16);
+      dst[0] = nib8_to_fp8<GRID>(r.aq[j].x);
+      dst[1] = nib8_to_fp8<GRID>(r.aq[j].y);
+      s.sa[blk * kBM + row] = r.as[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kBItems; ++j) {
+      const int i = tid + kThreads * j;
+      const int row = i >> 3, blk = i & 7;
+      uint2 *dst = reinterpret_cast<uint2 *>(s.b + row * kRowBytes + blk * 16);
+      dst[0] = nib8_to_fp8<GRID>(r.bq[j].x);
+      dst[1] = nib8_to_fp8<GRID>(r.bq[j].y);
+      s.sb[blk * kBN + row] = r.bs[j];
+    }
+  }
+
+  // One stage: 8 blocks x (4 MFMA + 64 scale products + 64 FMAs) per wave.
+  __device__ __forceinline__ static void compute(const Stage &s, floatx16 (&acc)[4]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+    floatx16 zero;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero[r] = 0.0f;
+    const uint8_t *pa = s.a + (wave * 32 + l32) * kRowBytes + 8 * half;
+    const uint8_t *pb = s.b + l32 * kRowBytes + 8 * half;
+    const float *psa = s.sa + wave * 32 + 4 * half;
+    const float *psb = s.sb + l32;
 #pragma unroll 1
-    for (int b = 0; b < kStageBlocks; ++b) {
-      const long af = *reinterpret_cast<const long *>(s_a + (wave * 32 + l32) * kRowBytes +
-                                                      b * 16 + 8 * half);
+    for (int b = 0; b < kSB; ++b) {
+      const long af = *reinterpret_cast<const long *>(pa + b * 16);
       floatx16 p[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const long bf = *reinterpret_cast<const long *>(s_b + (nt * 32 + l32) * kRowBytes +
-                                                        b * 16 + 8 * half);
+        const long bf = *reinterpret_cast<const long *>(pb + nt * 32 * kRowBytes + b * 16);
         p[nt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af, bf, zero, 0, 0, 0);
       }
       float sa[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 v =
-            *reinterpret_cast<const float4 *>(s_sa + b * kBM + wave * 32 + 8 * j + 4 * half);
+        const float4 v = *reinterpret_cast<const float4 *>(psa + b * kBM + 8 * j);
         sa[4 * j + 0] = v.x;
         sa[4 * j + 1] = v.y;
         sa[4 * j + 2] = v.z;
@@ -131,55 +184,79 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileJob &job,
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float sb = s_sb[b * kBN + nt * 32 + l32];
+        const float sb = psb[b * kBN + nt * 32];
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nt][r] = fmaf(sa[r] * sb, p[nt][r], acc[nt][r]);
       }
     }
-    __syncthreads();
   }
-  constexpr float inv_g2 = (GRID == kGridUniform) ? (1.0f / 49.0f) : (1.0f / 144.0f);
-  const int64_t m_rows = job.a_row_end - job.a_row0;
-  const int64_t n_cols = job.b_row_end - job.b_row0;
+
+  __device__ void run(Stage *stages) {
+    floatx16 acc[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n = nt * 32 + l32;
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (m < m_rows && n < n_cols) job.c[(int64_t)m * job.ldc + n] = acc[nt][r] * inv_g2;
+      for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+
+    const int64_t nstages = (job.kb1 - job.kb0 + kSB - 1) / kSB;
+    if (nstages > 0) {
+      Regs r;
+      load(r, job.kb0);
+      store(r, stages[0]);
+      __syncthreads();
+      for (int64_t st = 0; st < nstages; ++st) {
+        const bool more = st + 1 < nstages;
+        if (more) load(r, job.kb0 + (st + 1) * kSB);
+        compute(stages[st & 1], acc);
+        if (more) store(r, stages[(st + 1) & 1]);
+        __syncthreads();
+      }
+    }
+    constexpr float inv_g2 = (GRID == kGridUniform) ? (1.0f / 49.0f) : (1.0f / 144.0f);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = nt * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m < job.a_rows && n < job.b_rows) job.c[(int64_t)m * g.ldc + n] = acc[nt][r] * inv_g2;
+      }
     }
   }
-}
+};
 
 __device__ __forceinline__ int64_t clampv(int64_t v, int64_t n) {
   return v < 0 ? 0 : (v > n ? n : v);
 }
 
-// Group tables for the grouped modes: s_off = row offsets, s_pre = prefix of
-// per-group tile counts (mode 1) or padded K offsets (mode 2).
+// Group tables for the grouped modes: s_off = row offsets (clamped so no
+// access leaves the operands whatever the device array holds; a decreasing
+// pair is an empty group), s_pre = prefix of per-group tile counts (mode 1) or
+// of padded K lengths (mode 2).
+template <int MODE>
 __device__ void load_gemm_groups(const GemmArgs &g, int64_t *s_off, int64_t *s_pre,
                                  int64_t *s_scan) {
   const int tid = threadIdx.x;
   const int ng = g.n_groups;
-  const int per = (ng + 255) / 256;
+  const int per = (ng + kThreads - 1) / kThreads;
   const int g0 = tid * per;
   const int64_t tiles_n = (g.N + kBN - 1) / kBN;
-  // Offsets are clamped to [0, limit] (A rows in mode 1, padded K in mode 2
-  // is bounded separately) so no access leaves the operands whatever the
-  // device array holds; a decreasing pair is an empty group.
-  const int64_t limit = (g.mode == 1) ? g.M : INT64_MAX / 4;
+  const int64_t limit = (MODE == 1) ? g.M : (int64_t)1 << 40;
   int64_t local = 0;
   for (int e = g0; e < g0 + per && e < ng; ++e) {
     const int64_t a = clampv(g.goff[e], limit), b = clampv(g.goff[e + 1], limit);
     s_off[e] = a;
     const int64_t cnt = b > a ? b - a : 0;
-    local += (g.mode == 1) ? ((cnt + kBM - 1) / kBM) * tiles_n : (cnt + 15) / 16 * 16;
+    local += (MODE == 1) ? ((cnt + kBM - 1) / kBM) * tiles_n : (cnt + 15) / 16 * 16;
   }
   if (tid == 0) s_off[ng] = clampv(g.goff[ng], limit);
   s_scan[tid] = local;
   __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
+  for (int d = 1; d < kThreads; d <<= 1) {
     const int64_t add = tid >= d ? s_scan[tid - d] : 0;
     __syncthreads();
     s_scan[tid] += add;
@@ -190,45 +267,56 @@ __device__ void load_gemm_groups(const GemmArgs &g, int64_t *s_off, int64_t *s_p
     s_pre[e] = run;
     int64_t cnt = s_off[e + 1] - s_off[e];
     cnt = cnt > 0 ? cnt : 0;
-    run += (g.mode == 1) ? ((cnt + kBM - 1) / kBM) * tiles_n : (cnt + 15) / 16 * 16;
+    run += (MODE == 1) ? ((cnt + kBM - 1) / kBM) * tiles_n : (cnt + 15) / 16 * 16;
   }
-  if (tid == 255) s_pre[ng] = s_scan[255];
+  if (tid == kThreads - 1) s_pre[ng] = s_scan[kThreads - 1];
   __syncthreads();
 }
 
-template <int GRID>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[kBM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[kBN * kRowBytes];
-  __shared__ __attribute__((aligned(16))) float s_sa[kStageBlocks * kBM];
-  __shared__ __attribute__((aligned(16))) float s_sb[kStageBlocks * kBN];
-  __shared__ int64_t s_off[kMaxGemmGroups + 1];
-  __shared__ int64_t s_pre[kMaxGemmGroups + 1];
-  __shared__ int64_t s_scan[256];
+// XCD-major tile order: workgroups are dispatched to the 8 XCDs round robin,
+// so workgroup b runs on XCD b % 8; XCD x walks the contiguous tile range
+// [x * per, (x + 1) * per).
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t span) {
+  const int64_t per = span / kXcds;
+  return (b % kXcds) * per + b / kXcds;
+}
+
+template <int GRID, int MODE>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  Stage *stages = reinterpret_cast<Stage *>(smem);
+  int64_t *s_off = reinterpret_cast<int64_t *>(smem + 2 * sizeof(Stage));
+  int64_t *s_pre = s_off + (kMaxGemmGroups + 1);
+  int64_t *s_scan = s_pre + (kMaxGemmGroups + 1);
 
   const int64_t tiles_m = (g.M + kBM - 1) / kBM;
   const int64_t tiles_n = (g.N + kBN - 1) / kBN;
   const int64_t kblocks = g.kpad / 16;
-  if (g.mode != 0) load_gemm_groups(g, s_off, s_pre, s_scan);
+  if (MODE != 0) load_gemm_groups<MODE>(g, s_off, s_pre, s_scan);
 
   int64_t total;
-  if (g.mode == 0) total = tiles_m * tiles_n;
-  else if (g.mode == 1) total = s_pre[g.n_groups];
+  if (MODE == 0) total = tiles_m * tiles_n;
+  else if (MODE == 1) total = s_pre[g.n_groups];
   else total = (int64_t)g.n_groups * tiles_m * tiles_n;
+  // Iteration space: a multiple of both the grid and the XCD count, >= total.
+  const int64_t slots = (int64_t)gridDim.x;
+  const int64_t quantum = slots % kXcds == 0 ? slots : slots * kXcds;
+  const int64_t span = (total + quantum - 1) / quantum * quantum;
 
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+  for (int64_t b = blockIdx.x; b < span; b += slots) {
+    const int64_t t = xcd_tile(b, span);
+    if (t >= total) continue;
     TileJob job;
-    if (g.mode == 0) {
+    if (MODE == 0) {
       const int64_t tm = t / tiles_n, tn = t - tm * tiles_n;
       job.a_row0 = tm * kBM;
-      job.a_row_end = min(job.a_row0 + kBM, g.M);
+      job.a_rows = min((int64_t)kBM, g.M - job.a_row0);
       job.b_row0 = tn * kBN;
-      job.b_row_end = min(job.b_row0 + kBN, g.N);
+      job.b_rows = min((int64_t)kBN, g.N - job.b_row0);
       job.kb0 = 0;
       job.kb1 = kblocks;
       job.c = g.c + job.a_row0 * g.ldc + job.b_row0;
-      job.ldc = g.ldc;
-    } else if (g.mode == 1) {
+    } else if (MODE == 1) {
       int lo = 0, hi = g.n_groups;   // largest e with s_pre[e] <= t
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -238,29 +326,49 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
       const int64_t local = t - s_pre[e];
       const int64_t tm = local / tiles_n, tn = local - tm * tiles_n;
       job.a_row0 = s_off[e] + tm * kBM;
-      job.a_row_end = min(job.a_row0 + kBM, s_off[e + 1]);
+      job.a_rows = min((int64_t)kBM, s_off[e + 1] - job.a_row0);
       job.b_row0 = (int64_t)e * g.N + tn * kBN;
-      job.b_row_end = min(job.b_row0 + kBN, (int64_t)(e + 1) * g.N);
+      job.b_rows = min((int64_t)kBN, g.N - tn * kBN);
       job.kb0 = 0;
       job.kb1 = kblocks;
       job.c = g.c + job.a_row0 * g.ldc + tn * kBN;
-      job.ldc = g.ldc;
     } else {
       const int64_t per_group = tiles_m * tiles_n;
       const int64_t e = t / per_group;
       const int64_t local = t - e * per_group;
       const int64_t tm = local / tiles_n, tn = local - tm * tiles_n;
       job.a_row0 = tm * kBM;
-      job.a_row_end = min(job.a_row0 + kBM, g.M);
+      job.a_rows = min((int64_t)kBM, g.M - job.a_row0);
       job.b_row0 = tn * kBN;
-      job.b_row_end = min(job.b_row0 + kBN, g.N);
+      job.b_rows = min((int64_t)kBN, g.N - job.b_row0);
       job.kb0 = min(s_pre[e] / 16, kblocks);
       job.kb1 = min(s_pre[e + 1] / 16, kblocks);
       job.c = g.c + e * g.M * g.ldc + job.a_row0 * g.ldc + job.b_row0;
-      job.ldc = g.ldc;
     }
-    gemm_tile<GRID>(g, job, s_a, s_b, s_sa, s_sb);
+    Gemm<GRID> gm(g, job);
+    gm.run(stages);
+    __syncthreads();
   }
+}
+
+static size_t smem_bytes(int mode) {
+  size_t b = 2 * sizeof(Stage);
+  if (mode != 0) b += (2 * (kMaxGemmGroups + 1) + kThreads) * sizeof(int64_t);
+  return b;
+}
+
+template <int GRID, int MODE>
+static hipError_t launch_t(const GemmArgs &g, int64_t blocks, hipStream_t st) {
+  const size_t sm = smem_bytes(MODE);
+  static bool configured = false;
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<GRID, MODE>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL((gemm_kernel<GRID, MODE>), dim3((unsigned)blocks), dim3(kThreads), sm, st, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
@@ -272,11 +380,16 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
   else total = (int64_t)g.n_groups * tiles_m * tiles_n;
   int64_t blocks = total < 1 ? 1 : total;
   if (blocks > 65536) blocks = 65536;
-  if (g.grid == kGridUniform)
-    hipLaunchKernelGGL((gemm_kernel<kGridUniform>), dim3((unsigned)blocks), dim3(256), 0, st, g);
-  else
-    hipLaunchKernelGGL((gemm_kernel<kGridE2M1>), dim3((unsigned)blocks), dim3(256), 0, st, g);
-  return hipGetLastError();
+#define UFP4_G(GR, MO) return launch_t<GR, MO>(g, blocks, st)
+  if (g.grid == kGridUniform) {
+    if (g.mode == 0) UFP4_G(kGridUniform, 0);
+    if (g.mode == 1) UFP4_G(kGridUniform, 1);
+    UFP4_G(kGridUniform, 2);
+  }
+  if (g.mode == 0) UFP4_G(kGridE2M1, 0);
+  if (g.mode == 1) UFP4_G(kGridE2M1, 1);
+  UFP4_G(kGridE2M1, 2);
+#undef UFP4_G
 }
 
 }  // namespace ufp4

@@ -119,8 +119,9 @@ def ufp4_rht_quantize(x: torch.Tensor, axis: int = BLOCKS_ALONG_COLS, rht: bool 
                       sign_mask: int = 0, grid: int = GRID_UNIFORM, rnd: int = ROUND_RTNE,
                       seed: int = 0, stream_id: int = 0,
                       group_offsets: Optional[torch.Tensor] = None,
-                      kpad: Optional[int] = None) -> Quantized:
-    """Quantize a 2-D bf16 CUDA tensor (any row stride, unit column stride)."""
+                      kpad: Optional[int] = None, out: Optional[Quantized] = None) -> Quantized:
+    """Quantize a 2-D bf16 CUDA tensor (any row stride, unit column stride).
+    `out` reuses the buffers of an earlier result of the same shape."""
     assert x.dim() == 2 and x.dtype == torch.bfloat16 and x.is_cuda and x.stride(1) == 1
     n_rows, n_cols = x.shape
     n_groups = 0
@@ -134,8 +135,12 @@ def ufp4_rht_quantize(x: torch.Tensor, axis: int = BLOCKS_ALONG_COLS, rht: bool 
             kp = kpad if kpad is not None else padded_k_capacity(n_rows, n_groups)
         else:
             kp = (n_rows + 15) // 16 * 16
-    codes = torch.empty((rows, kp // 2), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((rows, kp // 16), dtype=torch.float32, device=x.device)
+    if out is not None:
+        assert out.rows == rows and out.kpad == kp
+        codes, scales = out.codes, out.scales
+    else:
+        codes = torch.empty((rows, kp // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, kp // 16), dtype=torch.float32, device=x.device)
     d = QTensorDesc(codes.data_ptr(), scales.data_ptr(), rows, 0, kp, 0, 0, 0, 0)
     st = lib().ufp4_rht_quantize(_ptr(x), n_rows, n_cols, x.stride(0), axis,
                                  _ptr(group_offsets), n_groups, int(rht), sign_mask, grid, rnd,
