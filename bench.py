@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--workload", default="dense-1.5b",
+                    choices=["dense-1.5b", "quant-sweep"],
+                    help="dense-1.5b: the timed step (default); quant-sweep: the 2^28-element "
+                         "quantizer sweep, one JSON line per case")
     return ap.parse_args()
 
 
@@ -160,8 +164,63 @@ def cpu_baseline(L, target_s: float):
     }
 
 
+def quant_sweep(args):
+    """The quantizer sweep: 16384 x 16384 bf16 (Gaussian, Laplace, Student-t3)
+    x {RHT, none} x {uniform, E2M1} x {RTNE, SR} x {row-wise, column-wise}.
+    Each case is timed with HIP events over `steps` calls after `warmup`; the
+    tensor (512 MiB) does not fit the 256 MiB MALL, so every call streams from
+    HBM.  Also reports 1 - alpha and SQNR of the dequantized (inverse-RHT)
+    tensor against the input, computed with torch reductions as diagnostics."""
+    import torch
+    from uniform_grid_fp4_amd import ufp4 as U
+    from uniform_grid_fp4_amd import workloads as W
+    dev = torch.device("cuda:0")
+    n = W.SWEEP_SHAPE[0] * W.SWEEP_SHAPE[1]
+    for dist in W.SWEEP_DISTS:
+        x = W.sweep_tensor(dist, dev)
+        xf = x.double()
+        ex = float((xf * xf).sum())
+        for axis in (U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS):
+            for rht in (True, False):
+                for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
+                    for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+                        q = U.ufp4_rht_quantize(x, axis, rht, 0xBEEF, grid, rnd, 7, 0)
+                        for _ in range(args.warmup):
+                            U.ufp4_rht_quantize(x, axis, rht, 0xBEEF, grid, rnd, 7, 0, out=q)
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                        for _ in range(args.steps):
+                            U.ufp4_rht_quantize(x, axis, rht, 0xBEEF, grid, rnd, 7, 0, out=q)
+                        e1.record()
+                        torch.cuda.synchronize()
+                        ms = e0.elapsed_time(e1) / args.steps
+                        xh = U.ufp4_dequantize(q, inverse_rht=rht).double()
+                        if axis == U.BLOCKS_ALONG_ROWS:
+                            xh = xh.t()
+                        dot = float((xh * xf).sum())
+                        err = float(((xh - xf) ** 2).sum())
+                        del xh
+                        gbs = n * BYTES_PER_QUANT_ELEM / (ms * 1e-3) / 1e9
+                        print(json.dumps({
+                            "workload": "quant-sweep", "dist": dist,
+                            "layout": ("colwise-transposed" if axis == U.BLOCKS_ALONG_ROWS
+                                       else "rowwise"),
+                            "rht": rht, "grid": "uniform" if grid == 0 else "e2m1",
+                            "rounding": "sr" if rnd else "rtne", "us": round(ms * 1e3, 2),
+                            "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "one_minus_alpha": dot and 1.0 - dot / ex,
+                            "sqnr_db": 10.0 * __import__("math").log10(ex / err)}), flush=True)
+        del x, xf
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.workload == "quant-sweep":
+        if args.gpus != 1:
+            sys.exit(2)
+        return quant_sweep(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the UFP4 hot path is "
               "data parallel and this build measures one GPU's share.", file=sys.stderr)

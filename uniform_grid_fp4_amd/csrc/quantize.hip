@@ -22,39 +22,99 @@ namespace ufp4 {
 //   CONTIG: ld == n_cols == kpad (whole input contiguous, no ragged tail).
 //   VEC:    16-byte loads (x 16-byte aligned, ld % 8 == 0), tail guarded.
 // ---------------------------------------------------------------------------
-template <int GRID, int RND, bool RHT, bool CONTIG, bool VEC>
+template <bool RHT>
+__device__ __forceinline__ void unpack16(const uint4 a0, const uint4 a1, uint32_t sign_mask,
+                                         float (&v)[16]) {
+  const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = bf16_lo(w[i], RHT ? sign_bit(sign_mask, 2 * i) : 0u);
+    v[2 * i + 1] = bf16_hi(w[i], RHT ? sign_bit(sign_mask, 2 * i + 1) : 0u);
+  }
+}
+
+// Contiguous input (ld == n_cols, n_cols % 16 == 0, 16-byte aligned): block b
+// is the 32 bytes at x + 16 b.  A wave owns 64 consecutive blocks (2 KiB) per
+// iteration and reads them with two fully coalesced 16-byte-per-lane loads
+// (lane l takes bytes 16l and 1024 + 16l); a round trip through LDS then gives
+// lane l its own block's 32 bytes.  The grid-stride loop is software
+// pipelined: the next chunk's loads are issued before the current chunk is
+// processed, and the last prefetch is clamped in range instead of branched.
+template <int GRID, int RND, bool RHT>
+__device__ __forceinline__ void quantize_store(const uint4 a0, const uint4 a1, int64_t b,
+                                               uint8_t *__restrict__ codes,
+                                               float *__restrict__ scales, uint32_t sign_mask,
+                                               uint32_t seed_lo, uint32_t seed_hi,
+                                               uint32_t stream_id) {
+  float v[16];
+  unpack16<RHT>(a0, a1, sign_mask, v);
+  uint32_t w0, w1;
+  float s;
+  quantize_block<GRID, RND, RHT>(v, (uint64_t)b * 16u, seed_lo, seed_hi, stream_id, w0, w1, s);
+  *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(w0, w1);
+  scales[b] = s;
+}
+
+template <int GRID, int RND, bool RHT>
+__global__ __launch_bounds__(256) void quant_rows_contig_kernel(
+    const uint16_t *__restrict__ x, int64_t nblk, uint8_t *__restrict__ codes,
+    float *__restrict__ scales, uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi,
+    uint32_t stream_id) {
+  __shared__ uint4 s_stage[4][128];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t nfull = nblk / 64;               // chunks of 64 whole blocks
+  const int64_t wstride = (int64_t)gridDim.x * 4;
+  const int64_t c0 = (int64_t)blockIdx.x * 4 + wave;
+  const uint4 *src = reinterpret_cast<const uint4 *>(x);
+  uint4 *st = s_stage[wave];
+  // Full chunks: no per-lane condition anywhere in the loop, so the compiler's
+  // wait counting never has to merge paths and only waits for the loads it
+  // needs (one iteration old), never for the stores in flight.
+  if (c0 < nfull) {
+    uint4 r0 = src[c0 * 128 + lane], r1 = src[c0 * 128 + 64 + lane];
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int64_t c = c0; c < nfull; c += wstride) {
+      const int64_t cn = min(c + wstride, nfull - 1);
+      const uint4 n0 = src[cn * 128 + lane], n1 = src[cn * 128 + 64 + lane];
+      st[lane] = r0;
+      st[64 + lane] = r1;
+      __builtin_amdgcn_wave_barrier();
+      const uint4 a0 = st[2 * lane], a1 = st[2 * lane + 1];
+      __builtin_amdgcn_wave_barrier();
+      quantize_store<GRID, RND, RHT>(a0, a1, c * 64 + lane, codes, scales, sign_mask, seed_lo,
+                                     seed_hi, stream_id);
+      r0 = n0;
+      r1 = n1;
+    }
+  }
+  // The ragged last chunk (fewer than 64 blocks), by one wave.
+  if (nblk % 64 != 0 && c0 == nfull % wstride) {
+    const int64_t b = nfull * 64 + lane;
+    if (b < nblk)
+      quantize_store<GRID, RND, RHT>(src[2 * b], src[2 * b + 1], b, codes, scales, sign_mask,
+                                     seed_lo, seed_hi, stream_id);
+  }
+}
+
+// General row-wise input (any stride, alignment or ragged tail): a 2-D
+// grid-stride loop over rows and 16-element blocks, so no division is needed;
+// VEC rows (16-byte aligned, ld % 8 == 0) use vector loads for full blocks.
+template <int GRID, int RND, bool RHT, bool VEC>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
     int64_t kblocks, uint8_t *__restrict__ codes, float *__restrict__ scales,
     uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id) {
-  const int64_t nblk = n_rows * kblocks;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-    float v[16];
-    if (CONTIG) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(x + b * 16);
-      const uint4 a0 = p[0];
-      const uint4 a1 = p[1];
-      const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = bf16_lo(w[i], RHT ? sign_bit(sign_mask, 2 * i) : 0u);
-        v[2 * i + 1] = bf16_hi(w[i], RHT ? sign_bit(sign_mask, 2 * i + 1) : 0u);
-      }
-    } else {
-      const int64_t row = b / kblocks;
-      const int64_t kb = b - row * kblocks;
+  for (int64_t row = blockIdx.y; row < n_rows; row += gridDim.y) {
+    const uint16_t *xr = x + row * ld;
+    for (int64_t kb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; kb < kblocks;
+         kb += (int64_t)gridDim.x * blockDim.x) {
       const int64_t c0 = kb * 16;
-      const uint16_t *p = x + row * ld + c0;
+      const uint16_t *p = xr + c0;
+      float v[16];
       if (VEC && c0 + 16 <= n_cols) {
-        const uint4 a0 = *reinterpret_cast<const uint4 *>(p);
-        const uint4 a1 = *reinterpret_cast<const uint4 *>(p + 8);
-        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          v[2 * i] = bf16_lo(w[i], RHT ? sign_bit(sign_mask, 2 * i) : 0u);
-          v[2 * i + 1] = bf16_hi(w[i], RHT ? sign_bit(sign_mask, 2 * i + 1) : 0u);
-        }
+        unpack16<RHT>(*reinterpret_cast<const uint4 *>(p), *reinterpret_cast<const uint4 *>(p + 8),
+                      sign_mask, v);
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -62,31 +122,40 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
           v[j] = bf16_lo(h, RHT ? sign_bit(sign_mask, j) : 0u);
         }
       }
+      const int64_t b = row * kblocks + kb;
+      uint32_t w0, w1;
+      float s;
+      quantize_block<GRID, RND, RHT>(v, (uint64_t)b * 16u, seed_lo, seed_hi, stream_id, w0, w1,
+                                     s);
+      *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(w0, w1);
+      scales[b] = s;
     }
-    uint32_t w0, w1;
-    float s;
-    quantize_block<GRID, RND, RHT>(v, (uint64_t)b * 16u, seed_lo, seed_hi, stream_id, w0, w1, s);
-    *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(w0, w1);
-    scales[b] = s;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Column-wise: blocks along the strided dimension, output transposed.
-// A workgroup owns a tile of 256 padded rows (16 blocks) x 64 columns.  Lane
-// (cp, rq) loads one dword (two adjacent columns) of 16 consecutive rows for
-// row-blocks rq and rq + 8, so every row of the tile is read as 128 contiguous
-// bytes; the four quantized blocks go to LDS and the tile is written back as
-// 64 output rows of 128 contiguous bytes of codes and 64 bytes of scales.
+// A workgroup (4 waves) owns a tile of 256 padded rows (16 blocks) x 128
+// columns.  Wave w quantizes row-blocks w, w+4, w+8, w+12; in each, lane l
+// loads one dword (columns 2l, 2l+1) of the 16 rows, so every row is read as
+// 256 contiguous bytes, and the block's rows come from one wave-uniform buffer
+// resource.  The quantized blocks go to LDS and the tile is written back as
+// 128 output rows of 128 contiguous bytes of codes and 64 bytes of scales.
 // Groups: padded block p belongs to the group e with P_e <= 16p < P_{e+1};
 // its rows are off_e + (16p - P_e) + j, zero past the group's end.
 // ---------------------------------------------------------------------------
 constexpr int kColTileRows = 256;
-constexpr int kColTileCols = 64;
+constexpr int kColTileCols = 128;
 constexpr int kMaxGroups = 1024;
 
 __device__ __forceinline__ int64_t clamp_rows(int64_t v, int64_t n) {
   return v < 0 ? 0 : (v > n ? n : v);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Prefix sums of the groups' padded lengths into LDS (block-wide scan).
@@ -146,64 +215,111 @@ __device__ __forceinline__ int find_group(const int64_t *s_poff, int n_groups, i
   return lo;
 }
 
-template <int GRID, int RND, bool RHT, bool VEC>
+// Raw dwords of one block of 16 rows for this lane's two columns.
+template <bool VEC>
+__device__ __forceinline__ void load_col_block(const uint16_t *__restrict__ x, int64_t ld,
+                                               int64_t n_cols, int64_t row0, int valid,
+                                               int col2, uint32_t keep, uint32_t (&w)[16]) {
+  // Rows past `valid`, and columns past n_cols in the last valid row, are
+  // outside the resource and read as zero; earlier rows' columns past n_cols
+  // are masked with `keep`.
+  const int64_t nbytes = valid > 0 ? ((int64_t)(valid - 1) * ld + n_cols) * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x + row0 * ld), (short)0, (int)nbytes, 0x00020000);
+  const int ld2 = (int)(ld * 2);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int off = j * ld2 + col2;
+    if (VEC) {
+      w[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0) & keep;
+    } else {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 2, 0, 0);
+      w[j] = (lo | (hi << 16)) & keep;
+    }
+  }
+}
+
+template <int GRID, int RND, bool RHT, bool VEC, bool GROUPED>
 __global__ __launch_bounds__(256) void quant_cols_kernel(
     const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
     const int64_t *__restrict__ goff, int n_groups, int64_t kpad, uint8_t *__restrict__ codes,
     float *__restrict__ scales, uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi,
     uint32_t stream_id) {
-  __shared__ int64_t s_off[kMaxGroups + 1];
-  __shared__ int64_t s_poff[kMaxGroups + 1];
-  __shared__ int64_t s_scan[256];
+  constexpr int kTabs = GROUPED ? kMaxGroups + 1 : 1;
+  __shared__ int64_t s_off[kTabs];
+  __shared__ int64_t s_poff[kTabs];
+  __shared__ int64_t s_scan[GROUPED ? 256 : 1];
   __shared__ uint2 s_codes[kColTileCols][kColTileRows / 16 + 1];
   __shared__ float s_scales[kColTileCols][kColTileRows / 16 + 1];
 
-  const int ng = goff ? n_groups : 1;
-  load_group_tables(goff, n_groups, n_rows, s_off, s_poff, s_scan);
+  int64_t padded_end;
+  if (GROUPED) {
+    load_group_tables(goff, n_groups, n_rows, s_off, s_poff, s_scan);
+    padded_end = s_poff[n_groups];
+  } else {
+    padded_end = (n_rows + 15) / 16 * 16;
+  }
 
   const int tid = threadIdx.x;
-  const int cp = tid & 31;   // column pair within the tile
-  const int rq = tid >> 5;   // 0..7
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t kblocks = kpad / 16;
   const int64_t n_ptiles = (kpad + kColTileRows - 1) / kColTileRows;
   const int64_t n_ctiles = (n_cols + kColTileCols - 1) / kColTileCols;
   const int64_t total = n_ptiles * n_ctiles;
-  const int64_t padded_end = s_poff[ng];
 
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int64_t pt = tile % n_ptiles;
-    const int64_t ct = tile / n_ptiles;
-    const int64_t pb0 = pt * (kColTileRows / 16);   // first padded block of the tile
-    const int64_t col0 = ct * kColTileCols;
-    const int64_t col = col0 + 2 * cp;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int rb = rq + 8 * half;                   // block within the tile
-      const int64_t p = pb0 + rb;                     // padded block index
-      float va[16], vb[16];
-      int64_t row0 = 0;
-      int valid = 0;
-      if (p < kblocks && 16 * p < padded_end) {
-        const int e = find_group(s_poff, ng, 16 * p);
+  // Row range of padded block p: [row0, row0 + valid), wave-uniform.
+  auto block_rows = [&](int64_t p, int64_t &row0, int &valid) {
+    row0 = 0;
+    valid = 0;
+    if (p < kblocks && 16 * p < padded_end) {
+      if (GROUPED) {
+        const int e = find_group(s_poff, n_groups, 16 * p);
         row0 = s_off[e] + (16 * p - s_poff[e]);
         const int64_t left = s_off[e + 1] - row0;
         valid = left >= 16 ? 16 : (int)(left > 0 ? left : 0);
+      } else {
+        row0 = 16 * p;
+        const int64_t left = n_rows - row0;
+        valid = left >= 16 ? 16 : (int)left;
       }
+    }
+    row0 = uniform64(row0);
+    valid = __builtin_amdgcn_readfirstlane(valid);
+  };
+
+  // Column tiles vary fastest, so the workgroups in flight together cover
+  // whole input rows (contiguous DRAM pages) rather than a narrow strip of
+  // many rows.
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int64_t pt = tile / n_ctiles;
+    const int64_t ct = tile - pt * n_ctiles;
+    const int64_t pb0 = pt * (kColTileRows / 16);   // first padded block of the tile
+    const int64_t col0 = ct * kColTileCols;
+    const int64_t col = col0 + 2 * lane;
+    const uint32_t keep = (col + 1 < n_cols) ? 0xFFFFFFFFu : (col < n_cols ? 0x0000FFFFu : 0u);
+    const int col2 = (int)(col * 2);
+    // Wave w quantizes row-blocks w, w+4, w+8, w+12 of the tile; the loads of
+    // the next row-block are in flight while the current one is quantized.
+    uint32_t cur[16], nxt[16];
+    int64_t row0;
+    int valid;
+    block_rows(pb0 + wave, row0, valid);
+    load_col_block<VEC>(x, ld, n_cols, row0, valid, col2, keep, cur);
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+      const int rb = wave + 4 * q;                    // block within the tile (wave-uniform)
+      const int64_t p = pb0 + rb;                     // padded block index
+      if (q < 3) {
+        block_rows(p + 4, row0, valid);
+        load_col_block<VEC>(x, ld, n_cols, row0, valid, col2, keep, nxt);
+      }
+      float va[16], vb[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        uint32_t w = 0u;
-        if (j < valid) {
-          const uint16_t *q = x + (row0 + j) * ld + col;
-          if (VEC && col + 1 < n_cols) {
-            w = *reinterpret_cast<const uint32_t *>(q);
-          } else {
-            const uint32_t a = col < n_cols ? (uint32_t)q[0] : 0u;
-            const uint32_t b = col + 1 < n_cols ? (uint32_t)q[1] : 0u;
-            w = a | (b << 16);
-          }
-        }
-        va[j] = bf16_lo(w, RHT ? sign_bit(sign_mask, j) : 0u);
-        vb[j] = bf16_hi(w, RHT ? sign_bit(sign_mask, j) : 0u);
+        va[j] = bf16_lo(cur[j], RHT ? sign_bit(sign_mask, j) : 0u);
+        vb[j] = bf16_hi(cur[j], RHT ? sign_bit(sign_mask, j) : 0u);
       }
       uint32_t a0, a1, b0, b1;
       float sa, sb;
@@ -211,25 +327,33 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       const uint64_t base_b = base_a + (uint64_t)kpad;
       quantize_block<GRID, RND, RHT>(va, base_a, seed_lo, seed_hi, stream_id, a0, a1, sa);
       quantize_block<GRID, RND, RHT>(vb, base_b, seed_lo, seed_hi, stream_id, b0, b1, sb);
-      s_codes[2 * cp][rb] = make_uint2(a0, a1);
-      s_codes[2 * cp + 1][rb] = make_uint2(b0, b1);
-      s_scales[2 * cp][rb] = sa;
-      s_scales[2 * cp + 1][rb] = sb;
+      s_codes[2 * lane][rb] = make_uint2(a0, a1);
+      s_codes[2 * lane + 1][rb] = make_uint2(b0, b1);
+      s_scales[2 * lane][rb] = sa;
+      s_scales[2 * lane + 1][rb] = sb;
+      if (q < 3) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+      }
     }
     __syncthreads();
-    // write back: 64 columns x 16 blocks of 8-byte codes, lane -> (column, block)
+    // write back: 128 columns x 16 blocks of 8-byte codes; 16 consecutive
+    // lanes write one column's 128 contiguous bytes
     const int nb = (int)((kblocks - pb0) < 16 ? (kblocks - pb0) : 16);
+    const int blk = tid & 15;
+    const int c0 = tid >> 4;                           // 0..15, then +16 per step
+    uint8_t *dq = codes + (col0 + c0) * (kpad / 2) + (pb0 + blk) * 8;
+    float *ds = scales + (col0 + c0) * kblocks + pb0 + blk;
+    const int64_t step_q = 16 * (kpad / 2), step_s = 16 * kblocks;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = tid + 256 * it;      // 0..1023
-      const int c = i >> 4;
-      const int blk = i & 15;
-      const int64_t oc = col0 + c;
-      if (oc < n_cols && blk < nb) {
-        uint2 *dst = reinterpret_cast<uint2 *>(codes + oc * (kpad / 2) + (pb0 + blk) * 8);
-        *dst = s_codes[c][blk];
-        scales[oc * kblocks + pb0 + blk] = s_scales[c][blk];
+    for (int it = 0; it < 8; ++it) {
+      const int c = c0 + 16 * it;
+      if (col0 + c < n_cols && blk < nb) {
+        *reinterpret_cast<uint2 *>(dq) = s_codes[c][blk];
+        *ds = s_scales[c][blk];
       }
+      dq += step_q;
+      ds += step_s;
     }
     __syncthreads();
   }
@@ -307,22 +431,24 @@ static int grid_for(int64_t work_items, int per_block, int max_blocks) {
 template <int GRID, int RND, bool RHT>
 static hipError_t launch_rows_t(const QuantArgs &a, hipStream_t st) {
   const int64_t kblocks = a.kpad / 16;
-  const int64_t nblk = a.n_rows * kblocks;
-  const int blocks = grid_for(nblk, 256, 256 * 16);
-  const bool contig = (a.ld == a.n_cols) && (a.n_cols % 16 == 0) &&
-                      ((reinterpret_cast<uintptr_t>(a.x) & 15u) == 0);
-  const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 15u) == 0) && (a.ld % 8 == 0);
-  if (contig)
-    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, true, true>), dim3(blocks), dim3(256), 0,
-                       st, a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
-                       a.seed_lo, a.seed_hi, a.stream_id);
-  else if (vec)
-    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, false, true>), dim3(blocks), dim3(256), 0,
-                       st, a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
+  if (aligned && a.ld == a.n_cols && a.n_cols % 16 == 0) {
+    const int64_t nblk = a.n_rows * kblocks;
+    const int blocks = grid_for(nblk, 256, 256 * 8);
+    hipLaunchKernelGGL((quant_rows_contig_kernel<GRID, RND, RHT>), dim3(blocks), dim3(256), 0, st,
+                       a.x, nblk, a.codes, a.scales, a.sign_mask, a.seed_lo, a.seed_hi,
+                       a.stream_id);
+    return hipGetLastError();
+  }
+  const int gx = grid_for(kblocks, 256, 64);
+  const int gy = (int)(a.n_rows < 8192 ? a.n_rows : 8192);
+  if (aligned && a.ld % 8 == 0)
+    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, true>), dim3(gx, gy), dim3(256), 0, st,
+                       a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
                        a.seed_lo, a.seed_hi, a.stream_id);
   else
-    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, false, false>), dim3(blocks), dim3(256), 0,
-                       st, a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
+    hipLaunchKernelGGL((quant_rows_kernel<GRID, RND, RHT, false>), dim3(gx, gy), dim3(256), 0, st,
+                       a.x, a.n_rows, a.n_cols, a.ld, kblocks, a.codes, a.scales, a.sign_mask,
                        a.seed_lo, a.seed_hi, a.stream_id);
   return hipGetLastError();
 }
@@ -332,15 +458,21 @@ static hipError_t launch_cols_t(const QuantArgs &a, hipStream_t st) {
   const int64_t n_ptiles = (a.kpad + kColTileRows - 1) / kColTileRows;
   const int64_t n_ctiles = (a.n_cols + kColTileCols - 1) / kColTileCols;
   const int blocks = grid_for(n_ptiles * n_ctiles, 1, 256 * 8);
-  const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0);
-  if (vec)
-    hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, true>), dim3(blocks), dim3(256), 0, st,
-                       a.x, a.n_rows, a.n_cols, a.ld, a.goff, a.n_groups, a.kpad, a.codes,
-                       a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id);
-  else
-    hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, false>), dim3(blocks), dim3(256), 0, st,
-                       a.x, a.n_rows, a.n_cols, a.ld, a.goff, a.n_groups, a.kpad, a.codes,
-                       a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id);
+  // dword loads need 4-byte aligned rows and an even column count (a dword
+  // straddling the last column of the last row would read as zero)
+  const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0) &&
+                   (a.n_cols % 2 == 0);
+#define UFP4_QC(V, G)                                                                          \
+  hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, V, G>), dim3(blocks), dim3(256), 0, st, \
+                     a.x, a.n_rows, a.n_cols, a.ld, a.goff, a.n_groups, a.kpad, a.codes,        \
+                     a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id)
+  const bool grouped = a.goff != nullptr;
+  if (vec) {
+    if (grouped) UFP4_QC(true, true); else UFP4_QC(true, false);
+  } else {
+    if (grouped) UFP4_QC(false, true); else UFP4_QC(false, false);
+  }
+#undef UFP4_QC
   return hipGetLastError();
 }
 

@@ -36,8 +36,9 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-input xors in one v_bitop3_b32 each (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -89,13 +90,6 @@ __device__ __forceinline__ void fwht16(float (&v)[16]) {
 // ---------------------------------------------------------------------------
 // Rounding a normalised value t (|t| <= g up to one ulp) to a magnitude index.
 // ---------------------------------------------------------------------------
-// Uniform grid, RTNE: nearest integer, ties to even.  Adding 1.5 * 2^23 puts
-// the value in a binade whose ulp is 1, so the FP32 add rounds half to even;
-// the low mantissa bits are then the integer.  |t| <= 7 + ulp rounds to 7.
-__device__ __forceinline__ uint32_t uniform_rtne(float m) {
-  return __float_as_uint(m + 12582912.0f) - 0x4B400000u;
-}
-
 // E2M1 grid {0,.5,1,1.5,2,3,4,6}, RTNE with ties to the even index: within
 // each binade the spacing is constant (0.5 below 2, 1 on [2,4), 2 on [4,6]),
 // so the same magic-constant add at that binade's spacing rounds half to even,
@@ -108,16 +102,8 @@ __device__ __forceinline__ uint32_t e2m1_rtne(float m) {
   return (__float_as_uint(m + magic) - __float_as_uint(magic)) + off;
 }
 
-// Stochastic rounding: lo = largest level <= m, f = position of m between lo
-// and the next level (exact), round up iff u < floor(f * 2^32).
-__device__ __forceinline__ uint32_t uniform_sr(float m, uint32_t u) {
-  m = fminf(m, 7.0f);
-  const float fl = floorf(m);
-  const float f = m - fl;                              // exact
-  const uint32_t F = (uint32_t)(f * 4294967296.0f);    // exact product, truncation = floor
-  return (uint32_t)fl + (u < F ? 1u : 0u);
-}
-
+// Stochastic rounding on E2M1: lo = largest level <= m, f = position of m
+// between lo and the next level (exact), round up iff u < floor(f * 2^32).
 __device__ __forceinline__ uint32_t e2m1_sr(float m, uint32_t u) {
   m = fminf(m, 6.0f);
   const bool lo = m < 2.0f;
@@ -131,9 +117,42 @@ __device__ __forceinline__ uint32_t e2m1_sr(float m, uint32_t u) {
   return (uint32_t)fl + off + (u < F ? 1u : 0u);
 }
 
-// Nibble: sign << 3 | index, and a zero index is always nibble 0.
-__device__ __forceinline__ uint32_t nibble(float t, uint32_t idx) {
-  return idx ? (((__float_as_uint(t) >> 28) & 8u) | idx) : 0u;
+// ---------------------------------------------------------------------------
+// Packing eight results into one word of nibbles (element 2i in the low
+// nibble of byte i), SWAR style.
+// ---------------------------------------------------------------------------
+// Byte 0 of each of four registers -> one word [b0(a) b0(b) b0(c) b0(d)].
+__device__ __forceinline__ uint32_t gather_b0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_amdgcn_perm(b, a, 0x0C0C0400u) | __builtin_amdgcn_perm(d, c, 0x04000C0Cu);
+}
+// Byte 3 of each of four registers.
+__device__ __forceinline__ uint32_t gather_b3(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_amdgcn_perm(b, a, 0x0C0C0703u) | __builtin_amdgcn_perm(d, c, 0x07030C0Cu);
+}
+// Even elements' low nibbles in the low halves of the bytes, odd elements' in
+// the high halves: byte i = e[i] & 15 | (o[i] & 15) << 4.
+__device__ __forceinline__ uint32_t interleave_nibbles(uint32_t even, uint32_t odd) {
+  return (even & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
+}
+// Sign word: bit 7 of byte i of se/so (sign of element 2i / 2i+1) moved to
+// bit 3 / bit 7 of byte i.
+__device__ __forceinline__ uint32_t interleave_signs(uint32_t se, uint32_t so) {
+  return (so & 0x80808080u) | ((se >> 4) & 0x08080808u);
+}
+// Sign-magnitude nibbles with the zero rule: the sign bit survives only where
+// the magnitude is non-zero (m + 7 carries into bit 3 exactly when m >= 1,
+// and never into the next nibble since m <= 7).
+__device__ __forceinline__ uint32_t apply_signs(uint32_t mags, uint32_t signs) {
+  return (signs & (mags + 0x77777777u)) | mags;
+}
+// Four-bit two's complement nibbles (values -7..7) -> sign-magnitude.  A
+// negative nibble v has magnitude (~v & 15) + 1 <= 7 (no carry out); a zero
+// stays zero, so no negative zero can appear.
+__device__ __forceinline__ uint32_t twos_to_signmag(uint32_t w) {
+  const uint32_t sg = w & 0x88888888u;
+  const uint32_t one = sg >> 3;
+  const uint32_t mag = (w ^ (one * 15u)) + one;
+  return mag | sg;
 }
 
 // ---------------------------------------------------------------------------
@@ -182,23 +201,50 @@ __device__ __forceinline__ void quantize_block(float (&v)[16], uint64_t idx0, ui
       for (int j = 0; j < 4; ++j) rnd[4 * c + j] = o.w[j];
     }
   }
-  w0 = 0u;
-  w1 = 0u;
+  float t[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float t = v[j] * post;
-    const float m = fabsf(t);
-    uint32_t idx;
-    if (GRID == kGridUniform)
-      idx = (RND == kRoundSR) ? uniform_sr(m, rnd[j]) : uniform_rtne(m);
-    else
-      idx = (RND == kRoundSR) ? e2m1_sr(m, rnd[j]) : e2m1_rtne(m);
-    const uint32_t nib = nibble(t, idx);
-    if (j < 8)
-      w0 |= nib << (4 * j);
-    else
-      w1 |= nib << (4 * (j - 8));
+  for (int j = 0; j < 16; ++j) t[j] = v[j] * post;
+  uint32_t words[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float *th = t + 8 * h;
+    if (GRID == kGridUniform && RND == kRoundRTNE) {
+      // Signed round half to even of t: adding 1.5 * 2^23 leaves round(t) in
+      // the low mantissa bits, as a two's complement byte.
+      uint32_t u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = __float_as_uint(th[j] + 12582912.0f);
+      const uint32_t w = interleave_nibbles(gather_b0(u[0], u[2], u[4], u[6]),
+                                            gather_b0(u[1], u[3], u[5], u[7]));
+      words[h] = twos_to_signmag(w);
+    } else {
+      uint32_t k[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float m = fabsf(th[j]);
+        const uint32_t r = rnd[8 * h + j];
+        if (GRID == kGridUniform) {
+          // k = floor(m) + (r < F), as an integer in byte 0 of floor(m) + 1.5*2^23
+          const float mc = fminf(m, 7.0f);
+          const float fl = floorf(mc);
+          const uint32_t F = (uint32_t)((mc - fl) * 4294967296.0f);
+          k[j] = __float_as_uint(fl + 12582912.0f) + (r < F ? 1u : 0u);
+        } else {
+          k[j] = (RND == kRoundSR) ? e2m1_sr(m, r) : e2m1_rtne(m);
+        }
+      }
+      const uint32_t mags = interleave_nibbles(gather_b0(k[0], k[2], k[4], k[6]),
+                                               gather_b0(k[1], k[3], k[5], k[7]));
+      const uint32_t signs = interleave_signs(
+          gather_b3(__float_as_uint(th[0]), __float_as_uint(th[2]), __float_as_uint(th[4]),
+                    __float_as_uint(th[6])),
+          gather_b3(__float_as_uint(th[1]), __float_as_uint(th[3]), __float_as_uint(th[5]),
+                    __float_as_uint(th[7])));
+      words[h] = apply_signs(mags, signs);
+    }
   }
+  w0 = words[0];
+  w1 = words[1];
 }
 
 }  // namespace ufp4
