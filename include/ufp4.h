@@ -78,7 +78,16 @@ typedef enum { UFP4_ROUND_RTNE = 0, UFP4_ROUND_SR = 1 } ufp4_round;
  *  ALONG_ROWS: the strided dimension; the output is transposed (output row j
  *              = input column j) and contiguous along the blocked dimension,
  *              the K-contiguous layout every GEMM below consumes. */
-typedef enum { UFP4_BLOCKS_ALONG_COLS = 0, UFP4_BLOCKS_ALONG_ROWS = 1 } ufp4_axis;
+/*  ALONG_ROWS_STACKED: the rows form n_groups equal groups (expert weights
+ *              W_e stacked along rows); each group is quantized as ALONG_ROWS
+ *              on its own and the transposed outputs are stacked: group e
+ *              fills output rows [e * n_cols, (e + 1) * n_cols).  This builds
+ *              the per-expert W_e^T operands of the grouped DGRAD. */
+typedef enum {
+  UFP4_BLOCKS_ALONG_COLS = 0,
+  UFP4_BLOCKS_ALONG_ROWS = 1,
+  UFP4_BLOCKS_ALONG_ROWS_STACKED = 2
+} ufp4_axis;
 
 /* A quantized operand.  Caller-owned device buffers:
  *   codes  [rows, kpad/2] bytes, byte j of a row = nib[2j] | nib[2j+1] << 4,
@@ -109,14 +118,17 @@ typedef struct {
  * axis: ufp4_axis.  ALONG_COLS: out->rows = n_rows, out->kpad =
  *   roundup16(n_cols), zero-padded.  ALONG_ROWS: out->rows = n_cols, the
  *   contraction runs over input rows.
- * d_group_offsets / n_groups (ALONG_ROWS only; NULL and 0 otherwise): device
+ * ALONG_ROWS_STACKED: d_group_offsets must be NULL, n_groups >= 1 divides
+ *   n_rows; out->rows = n_groups * n_cols, out->kpad = roundup16(n_rows /
+ *   n_groups); the SR index is that of the stacked output layout.
+ * d_group_offsets / n_groups (ALONG_ROWS only; NULL and 0 for ALONG_COLS): device
  *   int64 [n_groups+1] non-decreasing row offsets, first 0, last n_rows, that
  *   split the rows into groups (e.g. tokens per expert); every group is padded
  *   to a multiple of 16 on its own, so no block straddles two groups, and
  *   group e occupies columns [P_e, P_{e+1}) of the output with
  *   P_e = sum_{e'<e} roundup16(count_e').  out->kpad must be at least
  *   roundup16(n_rows + 15*n_groups); columns from P_{n_groups} to kpad are
- *   written as zeros.  NULL means one group.  1 <= n_groups <= 4096.
+ *   written as zeros.  NULL means one group.  1 <= n_groups <= 1024.
  * rht, sign_mask: apply y = (1/4) H16 D x per block (butterfly stages
  *   h = 1,2,4,8 in FP32, then the exact 1/4) with D from the mask.
  * grid, rnd, seed, stream_id: see the enums above (seed/stream_id ignored

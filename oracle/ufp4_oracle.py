@@ -60,6 +60,7 @@ ROUND_SR = 1
 
 AXIS_COLS = 0  # blocks along the contiguous (column) dimension, no transpose
 AXIS_ROWS = 1  # blocks along the strided (row) dimension, output transposed
+AXIS_ROWS_STACKED = 2  # equal row groups, each transposed on its own, stacked
 
 BLOCK = 16
 
@@ -193,7 +194,8 @@ def padded_offsets(group_offsets) -> np.ndarray:
     return np.concatenate([[0], np.cumsum([round_up16(c) for c in counts])]).astype(np.int64)
 
 
-def to_blocked_rows(x_f32: np.ndarray, axis: int, group_offsets=None) -> np.ndarray:
+def to_blocked_rows(x_f32: np.ndarray, axis: int, group_offsets=None,
+                    n_stack: int = 1) -> np.ndarray:
     """Arrange the input so that rows are output rows and the last axis is the
     padded contraction axis K_p; pads with +0.0.
 
@@ -202,7 +204,15 @@ def to_blocked_rows(x_f32: np.ndarray, axis: int, group_offsets=None) -> np.ndar
     axis == AXIS_ROWS: blocks along the strided dim; output row j is input
                        column j, and the contraction runs over input rows,
                        padded per group.
+    axis == AXIS_ROWS_STACKED: the rows are n_stack equal groups (e.g. expert
+                       weights stacked along rows); each is arranged as with
+                       AXIS_ROWS and the results are stacked along rows.
     """
+    if axis == AXIS_ROWS_STACKED:
+        n = x_f32.shape[0] // n_stack
+        assert n * n_stack == x_f32.shape[0]
+        return np.concatenate([to_blocked_rows(x_f32[e * n:(e + 1) * n], AXIS_ROWS)
+                               for e in range(n_stack)], axis=0)
     if axis == AXIS_COLS:
         rows, k = x_f32.shape
         kp = round_up16(k)
@@ -333,7 +343,7 @@ def unpack_nibbles(codes: np.ndarray) -> np.ndarray:
 
 def quantize(x_bits: np.ndarray, axis: int, rht: bool, sign_mask: int,
              grid: int, rnd: int, seed: int = 0, stream_id: int = 0,
-             group_offsets=None, kpad=None, out_rows=None):
+             group_offsets=None, kpad=None, out_rows=None, n_stack: int = 1):
     """Full quantizer on bf16 bit patterns [n_rows, n_cols].
 
     Returns (codes uint8 [rows, K_p/2], scales float32 [rows, K_p/16], K_p).
@@ -348,9 +358,10 @@ def quantize(x_bits: np.ndarray, axis: int, rht: bool, sign_mask: int,
     """
     x = bf16_bits_to_f32(x_bits)
     if out_rows is not None:
+        assert axis != AXIS_ROWS_STACKED
         out_rows = np.asarray(out_rows, dtype=np.int64)
         x = x[out_rows] if axis == AXIS_COLS else x[:, out_rows]
-    xb = to_blocked_rows(x, axis, group_offsets)
+    xb = to_blocked_rows(x, axis, group_offsets, n_stack)
     if kpad is not None and kpad > xb.shape[1]:
         xb = np.concatenate([xb, np.zeros((xb.shape[0], kpad - xb.shape[1]), np.float32)], 1)
     nib, s = quantize_blocked(xb, rht, sign_mask, grid, rnd, seed, stream_id, out_rows)

@@ -53,7 +53,7 @@ def quant(**kw):
     (dict(x=None), -1),
     (dict(out=fake_desc(codes=0)), -1),
     (dict(out=fake_desc(codes=0x1008)), -1),        # codes not 16-byte aligned
-    (dict(axis=2), -1), (dict(grid=5), -1), (dict(rnd=2), -1), (dict(rht=3), -1),
+    (dict(axis=5), -1), (dict(grid=5), -1), (dict(rnd=2), -1), (dict(rht=3), -1),
     (dict(mask=0x10000), -1),
     (dict(n_rows=0), -2), (dict(n_cols=-1), -2), (dict(ld=16), -2),
     (dict(out=fake_desc(kpad=48)), -2),             # row-wise kpad must be roundup16(n_cols)
@@ -62,6 +62,11 @@ def quant(**kw):
     (dict(axis=1, goff=FAKE, ng=0), -1),
     (dict(axis=1, goff=FAKE, ng=2000), -2),
     (dict(axis=1, goff=FAKE, ng=2, out=fake_desc(kpad=32)), -2),  # needs >= roundup16(32+30)
+    (dict(axis=3), -1),
+    (dict(axis=2, goff=FAKE, ng=2), -1),            # stacked takes no offsets
+    (dict(axis=2, ng=0), -2), (dict(axis=2, ng=3), -2),   # must divide n_rows
+    (dict(axis=2, ng=2, out=fake_desc(rows=32, kpad=16)), -2),   # rows must be 2 * 32
+    (dict(axis=2, ng=2, out=fake_desc(rows=64, kpad=32)), -2),   # kpad must be 16
 ])
 def test_quantize_rejects(kw, expect):
     assert quant(**kw) == expect

@@ -1,0 +1,167 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times: the dense 1.5B-model linear layer (tokens 8192, hidden 2048,
+FFN 8192), the MoE 7.9B-shaped expert layer (64 experts, hidden 2048, FFN
+1408, 16384 x top-6 routed rows) and one GPU's share of the MoE 124B-shaped
+layer (32 experts, hidden 6144, FFN 2048, 65536 x top-8 routed rows).
+
+The whole UFP4 recipe runs on the GPU (six quantizations, three GEMMs); the
+oracle checks sampled outputs it can compute one by one: quantized rows
+(bit-exact, SR included, using the SR row index of the full tensor), GEMM
+output rows, and for the grouped WGRAD sampled (expert, row, column)
+elements.  Tolerance for GEMMs: |err| <= 1e-5 * sum_k |a_k||b_k|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ufp4_oracle as O
+from uniform_grid_fp4_amd import ufp4 as U
+from uniform_grid_fp4_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SEED = 1234
+TOL = 1e-5
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=k)]))
+    return idx.astype(np.int64)
+
+
+def check_rows_quant(q, x, axis, mask, rnd, sid, rows, goff=None, what=""):
+    """Quantized rows `rows` of the GPU result equal the oracle's."""
+    if axis == U.BLOCKS_ALONG_COLS:
+        bits = W.bits_numpy(x[torch.as_tensor(rows, device=x.device)])
+        xb = O.to_blocked_rows(O.bf16_bits_to_f32(bits), O.AXIS_COLS)
+    else:
+        bits = W.bits_numpy(x[:, torch.as_tensor(rows, device=x.device)])
+        xb = O.to_blocked_rows(O.bf16_bits_to_f32(bits), O.AXIS_ROWS, goff)
+    if xb.shape[1] < q.kpad:
+        xb = np.concatenate([xb, np.zeros((xb.shape[0], q.kpad - xb.shape[1]), np.float32)], 1)
+    nib, s = O.quantize_blocked(xb, True, mask, O.GRID_UNIFORM, rnd, SEED, sid, row_ids=rows)
+    gc = host(q.codes[torch.as_tensor(rows, device=DEV)])
+    gs = host(q.scales[torch.as_tensor(rows, device=DEV)])
+    assert np.array_equal(gc, O.pack_nibbles(nib)), f"{what}: codes differ"
+    assert np.array_equal(gs.view(np.uint32), s.view(np.uint32)), f"{what}: scales differ"
+
+
+def deq_rows(q, rows):
+    r = torch.as_tensor(rows, device=DEV)
+    return O.dequantize64(host(q.codes[r]), host(q.scales[r]), O.GRID_UNIFORM)
+
+
+def assert_close(C, ref, bound, what):
+    err = np.abs(C.astype(np.float64) - ref)
+    bad = err > TOL * bound
+    assert not bad.any(), f"{what}: {bad.sum()} elements outside tolerance"
+
+
+def check_gemm_rows(C, a, b, rows, what, b_rows=None):
+    """Output rows `rows` of C = A B^T (B restricted to `b_rows` if given)."""
+    A = deq_rows(a, rows)
+    B = deq_rows(b, b_rows if b_rows is not None else np.arange(b.rows))
+    ref, bound = A @ B.T, np.abs(A) @ np.abs(B).T
+    assert_close(host(C[torch.as_tensor(rows, device=DEV)]), ref, bound, what)
+
+
+def test_dense_1p5b_layer():
+    L = W.dense_1p5b(DEV)
+    mf, md, mw = L.masks
+    T, H, F = L.x.shape[0], L.hidden, L.ffn
+    print("[fullsize] dense 1.5B layer", flush=True)
+    C, R = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS
+    xq = U.ufp4_rht_quantize(L.x, C, True, mf)
+    wq = U.ufp4_rht_quantize(L.w, C, True, mf)
+    dyq = U.ufp4_rht_quantize(L.dy, C, True, md, rnd=U.ROUND_SR, seed=SEED, stream_id=0)
+    wtq = U.ufp4_rht_quantize(L.w, R, True, md)
+    dytq = U.ufp4_rht_quantize(L.dy, R, True, mw, rnd=U.ROUND_SR, seed=SEED, stream_id=1)
+    xtq = U.ufp4_rht_quantize(L.x, R, True, mw)
+    y = U.ufp4_gemm_fprop(xq, wq)
+    dx = U.ufp4_gemm_dgrad(dyq, wtq)
+    dw = U.ufp4_gemm_wgrad(dytq, xtq)
+    torch.cuda.synchronize()
+    check_rows_quant(xq, L.x, C, mf, 0, 0, sample(T, 48, 1), what="X fprop")
+    check_rows_quant(wq, L.w, C, mf, 0, 0, sample(F, 48, 2), what="W fprop")
+    check_rows_quant(dyq, L.dy, C, md, 1, 0, sample(T, 48, 3), what="dY dgrad")
+    check_rows_quant(wtq, L.w, R, md, 0, 0, sample(H, 24, 4), what="W^T dgrad")
+    check_rows_quant(dytq, L.dy, R, mw, 1, 1, sample(F, 24, 5), what="dY^T wgrad")
+    check_rows_quant(xtq, L.x, R, mw, 0, 0, sample(H, 24, 6), what="X^T wgrad")
+    check_gemm_rows(y, xq, wq, sample(T, 12, 7), "fprop")
+    check_gemm_rows(dx, dyq, wtq, sample(T, 12, 8), "dgrad")
+    check_gemm_rows(dw, dytq, xtq, sample(F, 12, 9), "wgrad")
+
+
+def run_moe(L, n_q_rows, n_g_rows, n_elems):
+    mf, md, mw = L.masks
+    E, H, F = L.experts, L.hidden, L.ffn
+    off = L.offsets
+    T = int(off[-1])
+    offd = torch.as_tensor(off, device=DEV)
+    C, R, S = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS, U.BLOCKS_ALONG_ROWS_STACKED
+    xq = U.ufp4_rht_quantize(L.x, C, True, mf)
+    wq = U.ufp4_rht_quantize(L.w, C, True, mf)
+    dyq = U.ufp4_rht_quantize(L.dy, C, True, md, rnd=U.ROUND_SR, seed=SEED, stream_id=0)
+    wtq = U.ufp4_rht_quantize(L.w, S, True, md, n_groups=E)
+    dytq = U.ufp4_rht_quantize(L.dy, R, True, mw, rnd=U.ROUND_SR, seed=SEED, stream_id=1,
+                               group_offsets=offd)
+    xtq = U.ufp4_rht_quantize(L.x, R, True, mw, group_offsets=offd)
+    y = U.ufp4_grouped_gemm(U.FPROP, offd, xq, wq)
+    dx = U.ufp4_grouped_gemm(U.DGRAD, offd, dyq, wtq)
+    dw = U.ufp4_grouped_gemm(U.WGRAD, offd, dytq, xtq)
+    torch.cuda.synchronize()
+    assert y.shape == (T, F) and dx.shape == (T, H) and dw.shape == (E, F, H)
+    check_rows_quant(xq, L.x, C, mf, 0, 0, sample(T, n_q_rows, 11), what="X fprop")
+    check_rows_quant(dyq, L.dy, C, md, 1, 0, sample(T, n_q_rows, 13), what="dY dgrad")
+    check_rows_quant(dytq, L.dy, R, mw, 1, 1, sample(F, 8, 15), goff=off, what="dY^T wgrad")
+    check_rows_quant(xtq, L.x, R, mw, 0, 0, sample(H, 8, 16), goff=off, what="X^T wgrad")
+    # stacked W_e^T: expert e's rows [e*H, (e+1)*H) are the column-wise
+    # quantization of W_e with the stacked row index
+    for e in (0, E // 2, E - 1):
+        rows = sample(H, 6, 20 + e)
+        bits = W.bits_numpy(L.w[e * F:(e + 1) * F][:, torch.as_tensor(rows, device=DEV)])
+        xb = O.to_blocked_rows(O.bf16_bits_to_f32(bits), O.AXIS_ROWS)
+        nib, s = O.quantize_blocked(xb, True, md, O.GRID_UNIFORM, O.ROUND_RTNE)
+        r = torch.as_tensor(e * H + rows, device=DEV)
+        assert np.array_equal(host(wtq.codes[r]), O.pack_nibbles(nib)), f"W^T stacked e={e}"
+        assert np.array_equal(host(wtq.scales[r]).view(np.uint32), s.view(np.uint32))
+    # grouped FPROP / DGRAD rows: output row t uses its expert's B rows
+    for t in sample(T, n_g_rows, 17):
+        e = int(np.searchsorted(off, t, side="right") - 1)
+        check_gemm_rows(y, xq, wq, np.array([t]), f"grouped fprop row {t}",
+                        b_rows=np.arange(e * F, (e + 1) * F))
+        check_gemm_rows(dx, dyq, wtq, np.array([t]), f"grouped dgrad row {t}",
+                        b_rows=np.arange(e * H, (e + 1) * H))
+    # grouped WGRAD elements over each expert's padded token segment
+    poff = O.padded_offsets(off)
+    rng = np.random.default_rng(18)
+    counts = np.diff(off)
+    experts = [int(np.argmax(counts)), int(np.argmin(counts))] + list(rng.integers(0, E, 3))
+    for e in experts:
+        fr = np.unique(rng.integers(0, F, size=n_elems))
+        hr = np.unique(rng.integers(0, H, size=n_elems))
+        seg = slice(int(poff[e]), int(poff[e + 1]))
+        A = deq_rows(dytq, fr)[:, seg]
+        B = deq_rows(xtq, hr)[:, seg]
+        ref, bound = A @ B.T, np.abs(A) @ np.abs(B).T
+        got = host(dw[e][torch.as_tensor(fr, device=DEV)][:, torch.as_tensor(hr, device=DEV)])
+        assert_close(got, ref, bound, f"grouped wgrad expert {e}")
+    empty = np.where(counts == 0)[0]
+    for e in empty[:4]:
+        assert (host(dw[int(e)]) == 0).all()
+
+
+def test_moe_7p9b_layer():
+    print("[fullsize] MoE 7.9B expert layer", flush=True)
+    run_moe(W.moe_7p9b(DEV), 32, 6, 8)
+
+
+def test_moe_124b_layer_one_gpu_share():
+    print("[fullsize] MoE 124B expert layer, one GPU's share", flush=True)
+    run_moe(W.moe_124b(DEV), 16, 4, 6)
+    torch.cuda.empty_cache()

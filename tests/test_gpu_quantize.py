@@ -162,3 +162,19 @@ def test_quantize_is_deterministic():
     a = U.ufp4_rht_quantize(L.dy, U.BLOCKS_ALONG_ROWS, True, 99, 0, U.ROUND_SR, 5, 1)
     b = U.ufp4_rht_quantize(L.dy, U.BLOCKS_ALONG_ROWS, True, 99, 0, U.ROUND_SR, 5, 1)
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+
+
+@pytest.mark.parametrize("rnd", [U.ROUND_RTNE, U.ROUND_SR])
+@pytest.mark.parametrize("e,rows,cols", [(3, 40, 24), (5, 256, 130), (2, 300, 64)])
+def test_stacked_colwise(rnd, e, rows, cols):
+    g = torch.Generator(device=DEV).manual_seed(16)
+    x = torch.randn((e * rows, cols), device=DEV, generator=g).to(torch.bfloat16)
+    print(f"[quant] stacked e={e} rows={rows} cols={cols} rnd={rnd}", flush=True)
+    q = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_ROWS_STACKED, True, 0x5151, U.GRID_UNIFORM, rnd,
+                            9, 1, n_groups=e)
+    torch.cuda.synchronize()
+    c, s, kp = O.quantize(W.bits_numpy(x), O.AXIS_ROWS_STACKED, True, 0x5151, O.GRID_UNIFORM,
+                          rnd, 9, 1, n_stack=e)
+    assert q.kpad == kp and q.rows == e * cols and q.k == rows
+    assert np.array_equal(host(q.codes), c)
+    assert np.array_equal(host(q.scales).view(np.uint32), s.view(np.uint32))

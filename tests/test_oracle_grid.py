@@ -204,3 +204,25 @@ def test_row_subset_equals_rows_of_full_result(axis, rnd):
     assert kp3 == kp + 32 and (sk[:, -2:] == 0).all() and (ck[:, -16:] == 0).all()
     if rnd == O.ROUND_RTNE:
         assert (ck[:, :kp // 2] == cf).all()
+
+
+def test_stacked_axis_equals_per_group_transposes():
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((3 * 40, 24)).astype(np.float32)
+    b = (x.view(np.uint32) >> 16).astype(np.uint16)
+    for rnd in (O.ROUND_RTNE, O.ROUND_SR):
+        cs, ss, kp = O.quantize(b, O.AXIS_ROWS_STACKED, True, 0x0A0A, O.GRID_UNIFORM, rnd, 4, 1,
+                                n_stack=3)
+        assert cs.shape == (3 * 24, 24) and kp == 48
+        for e in range(3):
+            rows = slice(e * 24, (e + 1) * 24)
+            if rnd == O.ROUND_RTNE:
+                ce, se, _ = O.quantize(b[e * 40:(e + 1) * 40], O.AXIS_ROWS, True, 0x0A0A,
+                                       O.GRID_UNIFORM, rnd)
+                assert (cs[rows] == ce).all() and (ss[rows] == se).all()
+        # SR draws with the stacked output's row index: rows of the stacked
+        # result equal a column-wise quantization whose row ids are offset
+        xb = O.to_blocked_rows(O.bf16_bits_to_f32(b[40:80]), O.AXIS_ROWS)
+        nib, s1 = O.quantize_blocked(xb, True, 0x0A0A, O.GRID_UNIFORM, rnd, 4, 1,
+                                     row_ids=np.arange(24, 48))
+        assert (O.pack_nibbles(nib) == cs[24:48]).all() and (s1 == ss[24:48]).all()

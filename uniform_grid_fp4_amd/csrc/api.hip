@@ -71,7 +71,9 @@ ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_
     return UFP4_ERR_INVALID_ARG;
   if (!aligned16(out->codes) || !aligned16(out->scales) || out->reserved != 0)
     return UFP4_ERR_INVALID_ARG;
-  if (axis != UFP4_BLOCKS_ALONG_COLS && axis != UFP4_BLOCKS_ALONG_ROWS) return UFP4_ERR_INVALID_ARG;
+  if (axis != UFP4_BLOCKS_ALONG_COLS && axis != UFP4_BLOCKS_ALONG_ROWS &&
+      axis != UFP4_BLOCKS_ALONG_ROWS_STACKED)
+    return UFP4_ERR_INVALID_ARG;
   if (grid != UFP4_GRID_UNIFORM && grid != UFP4_GRID_E2M1) return UFP4_ERR_INVALID_ARG;
   if (rnd != UFP4_ROUND_RTNE && rnd != UFP4_ROUND_SR) return UFP4_ERR_INVALID_ARG;
   if (rht != 0 && rht != 1) return UFP4_ERR_INVALID_ARG;
@@ -84,10 +86,18 @@ ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_
     if (d_group_offsets != nullptr && (n_groups < 1 || n_groups > kMaxGroupsApi))
       return UFP4_ERR_SHAPE;
   }
+  if (axis == UFP4_BLOCKS_ALONG_ROWS_STACKED) {
+    if (d_group_offsets != nullptr) return UFP4_ERR_INVALID_ARG;
+    if (n_groups < 1 || n_rows % n_groups != 0) return UFP4_ERR_SHAPE;
+  }
   int64_t rows, kmin;
   if (axis == UFP4_BLOCKS_ALONG_COLS) {
     rows = n_rows;
     kmin = round_up16(n_cols);
+    if (out->kpad != kmin) return UFP4_ERR_SHAPE;
+  } else if (axis == UFP4_BLOCKS_ALONG_ROWS_STACKED) {
+    rows = n_cols * (int64_t)n_groups;
+    kmin = round_up16(n_rows / n_groups);
     if (out->kpad != kmin) return UFP4_ERR_SHAPE;
   } else {
     rows = n_cols;
@@ -116,7 +126,8 @@ ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_
   a.codes = out->codes;
   a.scales = out->scales;
   if (launch_quantize(a, stream) != hipSuccess) return UFP4_ERR_HIP;
-  out->k = (axis == UFP4_BLOCKS_ALONG_COLS) ? n_cols : n_rows;
+  out->k = (axis == UFP4_BLOCKS_ALONG_COLS) ? n_cols
+           : (axis == UFP4_BLOCKS_ALONG_ROWS_STACKED) ? n_rows / n_groups : n_rows;
   out->grid = grid;
   out->rht = rht;
   out->sign_mask = rht ? sign_mask : 0u;

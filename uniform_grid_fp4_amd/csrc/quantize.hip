@@ -240,12 +240,15 @@ __device__ __forceinline__ void load_col_block(const uint16_t *__restrict__ x, i
   }
 }
 
+// Stacked mode (n_stack > 1, not GROUPED): the input rows are n_stack equal
+// groups of n_rows rows, each quantized on its own and written as output rows
+// [s * n_cols, (s + 1) * n_cols).
 template <int GRID, int RND, bool RHT, bool VEC, bool GROUPED>
 __global__ __launch_bounds__(256) void quant_cols_kernel(
     const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
-    const int64_t *__restrict__ goff, int n_groups, int64_t kpad, uint8_t *__restrict__ codes,
-    float *__restrict__ scales, uint32_t sign_mask, uint32_t seed_lo, uint32_t seed_hi,
-    uint32_t stream_id) {
+    const int64_t *__restrict__ goff, int n_groups, int64_t n_stack, int64_t kpad,
+    uint8_t *__restrict__ codes, float *__restrict__ scales, uint32_t sign_mask,
+    uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id) {
   constexpr int kTabs = GROUPED ? kMaxGroups + 1 : 1;
   __shared__ int64_t s_off[kTabs];
   __shared__ int64_t s_poff[kTabs];
@@ -267,7 +270,8 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
   const int64_t kblocks = kpad / 16;
   const int64_t n_ptiles = (kpad + kColTileRows - 1) / kColTileRows;
   const int64_t n_ctiles = (n_cols + kColTileCols - 1) / kColTileCols;
-  const int64_t total = n_ptiles * n_ctiles;
+  const int64_t per_stack = n_ptiles * n_ctiles;
+  const int64_t total = per_stack * n_stack;
 
   // Row range of padded block p: [row0, row0 + valid), wave-uniform.
   auto block_rows = [&](int64_t p, int64_t &row0, int &valid) {
@@ -292,9 +296,13 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
   // Column tiles vary fastest, so the workgroups in flight together cover
   // whole input rows (contiguous DRAM pages) rather than a narrow strip of
   // many rows.
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  for (int64_t tile_all = blockIdx.x; tile_all < total; tile_all += gridDim.x) {
+    const int64_t si = tile_all / per_stack;
+    const int64_t tile = tile_all - si * per_stack;
     const int64_t pt = tile / n_ctiles;
     const int64_t ct = tile - pt * n_ctiles;
+    const uint16_t *xs = x + si * n_rows * ld;
+    const int64_t out_row0 = si * n_cols;          // first output row of this stack
     const int64_t pb0 = pt * (kColTileRows / 16);   // first padded block of the tile
     const int64_t col0 = ct * kColTileCols;
     const int64_t col = col0 + 2 * lane;
@@ -306,14 +314,14 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
     int64_t row0;
     int valid;
     block_rows(pb0 + wave, row0, valid);
-    load_col_block<VEC>(x, ld, n_cols, row0, valid, col2, keep, cur);
+    load_col_block<VEC>(xs, ld, n_cols, row0, valid, col2, keep, cur);
 #pragma unroll 1
     for (int q = 0; q < 4; ++q) {
       const int rb = wave + 4 * q;                    // block within the tile (wave-uniform)
       const int64_t p = pb0 + rb;                     // padded block index
       if (q < 3) {
         block_rows(p + 4, row0, valid);
-        load_col_block<VEC>(x, ld, n_cols, row0, valid, col2, keep, nxt);
+        load_col_block<VEC>(xs, ld, n_cols, row0, valid, col2, keep, nxt);
       }
       float va[16], vb[16];
 #pragma unroll
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       }
       uint32_t a0, a1, b0, b1;
       float sa, sb;
-      const uint64_t base_a = (uint64_t)col * (uint64_t)kpad + (uint64_t)p * 16u;
+      const uint64_t base_a = (uint64_t)(out_row0 + col) * (uint64_t)kpad + (uint64_t)p * 16u;
       const uint64_t base_b = base_a + (uint64_t)kpad;
       quantize_block<GRID, RND, RHT>(va, base_a, seed_lo, seed_hi, stream_id, a0, a1, sa);
       quantize_block<GRID, RND, RHT>(vb, base_b, seed_lo, seed_hi, stream_id, b0, b1, sb);
@@ -342,8 +350,8 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
     const int nb = (int)((kblocks - pb0) < 16 ? (kblocks - pb0) : 16);
     const int blk = tid & 15;
     const int c0 = tid >> 4;                           // 0..15, then +16 per step
-    uint8_t *dq = codes + (col0 + c0) * (kpad / 2) + (pb0 + blk) * 8;
-    float *ds = scales + (col0 + c0) * kblocks + pb0 + blk;
+    uint8_t *dq = codes + (out_row0 + col0 + c0) * (kpad / 2) + (pb0 + blk) * 8;
+    float *ds = scales + (out_row0 + col0 + c0) * kblocks + pb0 + blk;
     const int64_t step_q = 16 * (kpad / 2), step_s = 16 * kblocks;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -457,15 +465,17 @@ template <int GRID, int RND, bool RHT>
 static hipError_t launch_cols_t(const QuantArgs &a, hipStream_t st) {
   const int64_t n_ptiles = (a.kpad + kColTileRows - 1) / kColTileRows;
   const int64_t n_ctiles = (a.n_cols + kColTileCols - 1) / kColTileCols;
-  const int blocks = grid_for(n_ptiles * n_ctiles, 1, 256 * 8);
+  const int64_t n_stack = a.axis == 2 ? a.n_groups : 1;
+  const int64_t rows_per = a.n_rows / n_stack;
+  const int blocks = grid_for(n_ptiles * n_ctiles * n_stack, 1, 256 * 8);
   // dword loads need 4-byte aligned rows and an even column count (a dword
   // straddling the last column of the last row would read as zero)
   const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0) &&
                    (a.n_cols % 2 == 0);
 #define UFP4_QC(V, G)                                                                          \
   hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, V, G>), dim3(blocks), dim3(256), 0, st, \
-                     a.x, a.n_rows, a.n_cols, a.ld, a.goff, a.n_groups, a.kpad, a.codes,        \
-                     a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id)
+                     a.x, rows_per, a.n_cols, a.ld, a.goff, a.n_groups, n_stack, a.kpad,        \
+                     a.codes, a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id)
   const bool grouped = a.goff != nullptr;
   if (vec) {
     if (grouped) UFP4_QC(true, true); else UFP4_QC(true, false);

@@ -9,7 +9,7 @@ namespace ufp4 {
 struct QuantArgs {
   const uint16_t *x;
   int64_t n_rows, n_cols, ld;
-  int axis;                 // 0 blocks along columns, 1 along rows (transposed out)
+  int axis;                 // 0 along columns, 1 along rows (transposed), 2 stacked
   const int64_t *goff;      // device group offsets or nullptr
   int n_groups;
   int rht;

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libufp4.so")
 
 GRID_UNIFORM, GRID_E2M1 = 0, 1
 ROUND_RTNE, ROUND_SR = 0, 1
-BLOCKS_ALONG_COLS, BLOCKS_ALONG_ROWS = 0, 1
+BLOCKS_ALONG_COLS, BLOCKS_ALONG_ROWS, BLOCKS_ALONG_ROWS_STACKED = 0, 1, 2
 FPROP, DGRAD, WGRAD = 0, 1, 2
 
 STATUS = {0: "UFP4_OK", -1: "UFP4_ERR_INVALID_ARG", -2: "UFP4_ERR_SHAPE",
@@ -119,14 +119,20 @@ def ufp4_rht_quantize(x: torch.Tensor, axis: int = BLOCKS_ALONG_COLS, rht: bool 
                       sign_mask: int = 0, grid: int = GRID_UNIFORM, rnd: int = ROUND_RTNE,
                       seed: int = 0, stream_id: int = 0,
                       group_offsets: Optional[torch.Tensor] = None,
-                      kpad: Optional[int] = None, out: Optional[Quantized] = None) -> Quantized:
+                      kpad: Optional[int] = None, out: Optional[Quantized] = None,
+                      n_groups: int = 0) -> Quantized:
     """Quantize a 2-D bf16 CUDA tensor (any row stride, unit column stride).
-    `out` reuses the buffers of an earlier result of the same shape."""
+    `out` reuses the buffers of an earlier result of the same shape;
+    `n_groups` is the number of equal row groups for BLOCKS_ALONG_ROWS_STACKED."""
     assert x.dim() == 2 and x.dtype == torch.bfloat16 and x.is_cuda and x.stride(1) == 1
     n_rows, n_cols = x.shape
-    n_groups = 0
+    if axis != BLOCKS_ALONG_ROWS_STACKED:
+        n_groups = 0
     if axis == BLOCKS_ALONG_COLS:
         rows, kp = n_rows, (n_cols + 15) // 16 * 16
+    elif axis == BLOCKS_ALONG_ROWS_STACKED:
+        assert n_groups >= 1 and n_rows % n_groups == 0
+        rows, kp = n_cols * n_groups, (n_rows // n_groups + 15) // 16 * 16
     else:
         rows = n_cols
         if group_offsets is not None:
