@@ -45,9 +45,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--workload", default="dense-1.5b",
-                    choices=["dense-1.5b", "quant-sweep"],
+                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b"],
                     help="dense-1.5b: the timed step (default); quant-sweep: the 2^28-element "
-                         "quantizer sweep, one JSON line per case")
+                         "quantizer sweep, one JSON line per case; moe-*: the expert layers "
+                         "(grouped GEMMs), one JSON line")
     return ap.parse_args()
 
 
@@ -164,6 +165,66 @@ def cpu_baseline(L, target_s: float):
     }
 
 
+class MoeStep(Step):
+    """One pass of the hot path over an expert layer: X, W, dY quantized as in
+    the dense step, W^T per expert by the stacked column-wise quantization,
+    dY^T and X^T column-wise with per-expert padding, then the three grouped
+    GEMMs."""
+
+    def __init__(self, L, U, torch):
+        self.offd = torch.as_tensor(L.offsets, device=L.x.device)
+        self.E = L.experts
+        self.tokens = int(L.offsets[-1])
+        super().__init__(L, U, torch)
+
+    def quant(self, name, x, axis, mask, rnd, sid, ev, **kw):
+        U = self.U
+        if ev is not None:
+            ev[name][0].record()
+        q = U.ufp4_rht_quantize(x, axis, True, mask, U.GRID_UNIFORM, rnd, self.seed, sid,
+                                out=self.q.get(name), **kw)
+        if ev is not None:
+            ev[name][1].record()
+        self.q[name] = q
+        return q
+
+    def gemm(self, name, kind, a, b, out, ev):
+        if ev is not None:
+            ev[name][0].record()
+        self.U.ufp4_grouped_gemm(kind, self.offd, a, b, out=out)
+        if ev is not None:
+            ev[name][1].record()
+
+    def run(self, ev):
+        U, L = self.U, self.L
+        C, R, S = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS, U.BLOCKS_ALONG_ROWS_STACKED
+        if not hasattr(self, "dwg"):
+            T, H, F, E = self.tokens, self.H, self.F, self.E
+            dev = L.x.device
+            self.y = self.torch.empty((T, F), dtype=self.torch.float32, device=dev)
+            self.dx = self.torch.empty((T, H), dtype=self.torch.float32, device=dev)
+            self.dwg = self.torch.empty((E, F, H), dtype=self.torch.float32, device=dev)
+        xq = self.quant("q_x_fprop", L.x, C, self.mf, U.ROUND_RTNE, 0, ev)
+        wq = self.quant("q_w_fprop", L.w, C, self.mf, U.ROUND_RTNE, 0, ev)
+        self.gemm("fprop", U.FPROP, xq, wq, self.y, ev)
+        dyq = self.quant("q_dy_dgrad", L.dy, C, self.md, U.ROUND_SR, 0, ev)
+        wtq = self.quant("q_wt_dgrad", L.w, S, self.md, U.ROUND_RTNE, 0, ev, n_groups=self.E)
+        self.gemm("dgrad", U.DGRAD, dyq, wtq, self.dx, ev)
+        dytq = self.quant("q_dyt_wgrad", L.dy, R, self.mw, U.ROUND_SR, 1, ev,
+                          group_offsets=self.offd)
+        xtq = self.quant("q_xt_wgrad", L.x, R, self.mw, U.ROUND_RTNE, 0, ev,
+                         group_offsets=self.offd)
+        self.gemm("wgrad", U.WGRAD, dytq, xtq, self.dwg, ev)
+
+    def quant_elems(self):
+        T, H, F, E = self.tokens, self.H, self.F, self.E
+        return {"q_x_fprop": T * H, "q_w_fprop": E * F * H, "q_dy_dgrad": T * F,
+                "q_wt_dgrad": E * F * H, "q_dyt_wgrad": T * F, "q_xt_wgrad": T * H}
+
+    def gemm_flops(self):
+        return 2.0 * self.tokens * self.H * self.F
+
+
 def quant_sweep(args):
     """The quantizer sweep: 16384 x 16384 bf16 (Gaussian, Laplace, Student-t3)
     x {RHT, none} x {uniform, E2M1} x {RTNE, SR} x {row-wise, column-wise}.
@@ -231,8 +292,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    L = W.dense_1p5b(dev)
-    st = Step(L, U, torch)
+    if args.workload == "moe-7.9b":
+        L = W.moe_7p9b(dev)
+        st = MoeStep(L, U, torch)
+    elif args.workload == "moe-124b":
+        L = W.moe_124b(dev)
+        st = MoeStep(L, U, torch)
+    else:
+        L = W.dense_1p5b(dev)
+        st = Step(L, U, torch)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         st.run(None)
@@ -272,7 +340,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8-e4m3 MFMA operands (exact 4-bit levels), fp32 accumulate/scales",
         "data": "synthetic",
-        "config": {"workload": L.name, "tokens": st.T, "hidden": st.H, "ffn": st.F,
+        "config": {"workload": L.name, "tokens": int(L.offsets[-1]), "hidden": st.H,
+                   "ffn": st.F, "experts": L.experts,
                    "recipe": "UFP4: uniform grid, RHT-16 on all 3 GEMMs, SR on dY",
                    "block": 16, "scale": "fp32 absmax"},
         "quantize": {"gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
@@ -290,7 +359,7 @@ def main():
                      "frac": round(gemm_tflops / GEMM_ALU_PEAK_TFLOPS, 4),
                      "traffic": None},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "dense-1.5b":
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -239,7 +239,7 @@ __device__ __forceinline__ int64_t clampv(int64_t v, int64_t n) {
 // of padded K lengths (mode 2).
 template <int MODE>
 __device__ void load_gemm_groups(const GemmArgs &g, int64_t *s_off, int64_t *s_pre,
-                                 int64_t *s_scan) {
+                                 int64_t *s_scan, int *s_order) {
   const int tid = threadIdx.x;
   const int ng = g.n_groups;
   const int per = (ng + kThreads - 1) / kThreads;
@@ -271,6 +271,25 @@ __device__ void load_gemm_groups(const GemmArgs &g, int64_t *s_off, int64_t *s_p
   }
   if (tid == kThreads - 1) s_pre[ng] = s_scan[kThreads - 1];
   __syncthreads();
+  if (MODE == 2) {
+    // Largest group first: every tile of a group costs its group's K, so
+    // dispatching the heaviest groups' tiles first keeps the tail short.
+    // Rank by (count desc, index asc); O(ng^2) compares, only for ng <= 256.
+    for (int e = tid; e < ng; e += kThreads) {
+      if (ng <= 256) {
+        const int64_t ce = s_pre[e + 1] - s_pre[e];
+        int rank = 0;
+        for (int f = 0; f < ng; ++f) {
+          const int64_t cf = s_pre[f + 1] - s_pre[f];
+          rank += (cf > ce) || (cf == ce && f < e);
+        }
+        s_order[rank] = e;
+      } else {
+        s_order[e] = e;
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // XCD-major tile order: workgroups are dispatched to the 8 XCDs round robin,
@@ -288,11 +307,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   int64_t *s_off = reinterpret_cast<int64_t *>(smem + 2 * sizeof(Stage));
   int64_t *s_pre = s_off + (kMaxGemmGroups + 1);
   int64_t *s_scan = s_pre + (kMaxGemmGroups + 1);
+  int *s_order = reinterpret_cast<int *>(s_scan + kThreads);
 
   const int64_t tiles_m = (g.M + kBM - 1) / kBM;
   const int64_t tiles_n = (g.N + kBN - 1) / kBN;
   const int64_t kblocks = g.kpad / 16;
-  if (MODE != 0) load_gemm_groups<MODE>(g, s_off, s_pre, s_scan);
+  if (MODE != 0) load_gemm_groups<MODE>(g, s_off, s_pre, s_scan, s_order);
 
   int64_t total;
   if (MODE == 0) total = tiles_m * tiles_n;
@@ -304,7 +324,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   const int64_t span = (total + quantum - 1) / quantum * quantum;
 
   for (int64_t b = blockIdx.x; b < span; b += slots) {
-    const int64_t t = xcd_tile(b, span);
+    // Dense and M-grouped tiles all cost the same K, so each XCD takes a
+    // contiguous range (L2 reuse of A row panels); K-grouped tiles differ in
+    // cost by group, so they go round robin, heaviest group first.
+    const int64_t t = (MODE == 2) ? b : xcd_tile(b, span);
     if (t >= total) continue;
     TileJob job;
     if (MODE == 0) {
@@ -334,8 +357,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       job.c = g.c + job.a_row0 * g.ldc + tn * kBN;
     } else {
       const int64_t per_group = tiles_m * tiles_n;
-      const int64_t e = t / per_group;
-      const int64_t local = t - e * per_group;
+      const int64_t slot = t / per_group;
+      const int64_t local = t - slot * per_group;
+      const int64_t e = s_order[slot];
       const int64_t tm = local / tiles_n, tn = local - tm * tiles_n;
       job.a_row0 = tm * kBM;
       job.a_rows = min((int64_t)kBM, g.M - job.a_row0);
@@ -353,7 +377,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
 static size_t smem_bytes(int mode) {
   size_t b = 2 * sizeof(Stage);
-  if (mode != 0) b += (2 * (kMaxGemmGroups + 1) + kThreads) * sizeof(int64_t);
+  if (mode != 0)
+    b += (2 * (kMaxGemmGroups + 1) + kThreads) * sizeof(int64_t) + kMaxGemmGroups * sizeof(int);
   return b;
 }
 
