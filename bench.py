@@ -28,12 +28,42 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA
 # The GEMM is bound by its per-block FP32 rescale on the vector ALU: two VALU
 # operations (a multiply and an FMA) per output per 16-element block, i.e.
-# 2 ops per 16 MACs.  Non-packed FP32 VALU issue: 256 CU x 4 SIMD x 16 lanes
-# x 2.4 GHz = 39.32e12 lane-ops/s, so the GEMM ceiling is
-# 39.32e12 * 16 MAC / 2 ops * 2 FLOP/MAC = 629.1 TFLOP/s.
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# 2 ops per 16 MACs.  Non-packed FP32 VALU issue on gfx950: a wave64
+# instruction every 2 cycles per SIMD, i.e. 256 CU x 4 SIMD x 32 lanes x
+# 2.4 GHz = 78.64e12 lane-ops/s (the same unit count gives the published
+# 157.3 TFLOP/s FP32 vector FMA peak).  GEMM ceiling:
+# 78.64e12 * 16 MAC / 2 ops * 2 FLOP/MAC = 1258.3 TFLOP/s.
+VALU_LANE_OPS = 256 * 4 * 32 * 2.4e9
 GEMM_ALU_PEAK_TFLOPS = VALU_LANE_OPS * 16.0 / 2.0 * 2.0 / 1e12
 BYTES_PER_QUANT_ELEM = 2.0 + 0.5 + 0.25
+
+# HBM bytes per GEMM launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE
+# counters (averaged over the FPROP, DGRAD and WGRAD launches of one step),
+# each scaled by the factor that makes the same counter read the known size
+# of a plain 1 GiB device copy.  The figures hold for the GEMM source whose
+# SHA-256 is recorded with them; any other source reports null.
+GEMM_TRAFFIC = {
+    "dense-1.5B-fc1": {"sha256": "35e3e5bdfb5f32ef59efeeb45beaaf87939c0e114445fb3a55f5b74b70f8d512",
+                       "bytes_per_launch": 392836740},
+}
+GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
+                "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
+
+
+def gemm_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def gemm_traffic(workload: str):
+    rec = GEMM_TRAFFIC.get(workload)
+    if rec is None or rec["sha256"] != gemm_source_sha256():
+        return None
+    return rec["bytes_per_launch"]
 
 
 def parse():
@@ -45,10 +75,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--workload", default="dense-1.5b",
-                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b"],
+                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b", "copy"],
                     help="dense-1.5b: the timed step (default); quant-sweep: the 2^28-element "
                          "quantizer sweep, one JSON line per case; moe-*: the expert layers "
-                         "(grouped GEMMs), one JSON line")
+                         "(grouped GEMMs), one JSON line; copy: a plain 1 GiB device copy, the "
+                         "streaming ceiling and the calibration run of the HBM traffic "
+                         "counters")
     return ap.parse_args()
 
 
@@ -276,16 +308,42 @@ def quant_sweep(args):
         torch.cuda.empty_cache()
 
 
+def copy_ceiling(args):
+    """A plain contiguous 1 GiB device-to-device copy (torch's copy kernel):
+    the streaming ceiling the quantizer is compared with, and the run whose
+    FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures (it reads
+    and writes exactly 1 GiB per launch)."""
+    import torch
+    n = 1 << 29
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 2 * a.numel() * a.element_size()
+    print(json.dumps({"workload": "copy", "bytes_read": nbytes // 2, "bytes_written": nbytes // 2,
+                      "us": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}),
+          flush=True)
+
+
 def main():
     args = parse()
-    if args.workload == "quant-sweep":
-        if args.gpus != 1:
-            sys.exit(2)
-        return quant_sweep(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the UFP4 hot path is "
-              "data parallel and this build measures one GPU's share.", file=sys.stderr)
+              "data parallel and what is measured is one GPU's share of it.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "quant-sweep":
+        return quant_sweep(args)
+    if args.workload == "copy":
+        return copy_ceiling(args)
     import torch
     from uniform_grid_fp4_amd import ufp4 as U
     from uniform_grid_fp4_amd import workloads as W
@@ -353,11 +411,13 @@ def main():
                  "frac_fp8_mfma_peak": round(gemm_tflops / FP8_MFMA_PEAK_TFLOPS, 4),
                  "ms_per_step": round(g_ms, 4),
                  "per_call_ms": {n: round(dur[n], 4) for n in Step.GEMMS}},
-        "roofline": {"kernel": "ufp4::gemm_kernel<0>", "bound": "alu",
+        "roofline": {"kernel": ("ufp4::gemm_kernel<0, 1|2>" if isinstance(st, MoeStep)
+                                else "ufp4::gemm_kernel<0, 0>"),
+                     "bound": "alu",
                      "achieved": round(gemm_tflops, 2), "peak": round(GEMM_ALU_PEAK_TFLOPS, 1),
                      "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / GEMM_ALU_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": gemm_traffic(L.name)},
     }
     if not args.no_cpu_baseline and args.workload == "dense-1.5b":
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)

@@ -17,14 +17,19 @@
 // on the same SIMD.  Nibbles are expanded to FP8 (v_perm_b32 look-up) once per
 // workgroup while staging into LDS, so the waves read ready MFMA operands.
 //
-// Tiling: 512 threads = 8 waves, 256 x 128 output tile; wave w owns rows
-// [32w, 32w+32) x 128 columns = four 32x32 MFMA tiles sharing one A fragment
-// and one set of 16 row scales per block.  K advances 128 (8 blocks) per LDS
-// stage, double-buffered: the global loads of stage s+1 are in flight while
-// stage s is computed, and there is one barrier per stage.  Operands are read
-// with buffer loads whose range check returns zero past the tile's rows, so
-// ragged edges need no branches.  Tiles are assigned XCD-major: the 8 XCDs
-// each walk a contiguous range of tiles, so a row panel of A stays in one L2.
+// Tiling: 512 threads = 8 waves, 128 x 128 output tile; the waves form a
+// 4 x 2 grid and wave (wm, wn) owns rows [32wm, 32wm+32) x columns
+// [64wn, 64wn+64) = two 32x32 MFMA tiles sharing one A fragment and one set
+// of 16 row scales per block.  The kernel is built for 4 waves per SIMD (at
+// most 128 VGPRs, two workgroups per CU): the rescale issues one VALU
+// instruction per wave only every ~5 cycles, so a SIMD needs several waves
+// ready to keep its vector ALU busy while others wait on MFMA results, LDS
+// or the barrier.  K advances 64 (4 blocks) per LDS stage, double-buffered:
+// the global loads of stage s+1 are in flight while stage s is computed, and
+// there is one barrier per stage.  Operands are read with buffer loads whose
+// range check returns zero past the tile's rows, so ragged edges need no
+// branches.  Tiles are assigned XCD-major: the 8 XCDs each walk a contiguous
+// range of tiles, so a row panel of A stays in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,12 +41,17 @@ namespace ufp4 {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;
-constexpr int kBM = 256;
-constexpr int kBN = 128;
-constexpr int kSB = 8;                        // 16-element blocks per stage
+constexpr int kWavesM = 4;                    // waves along M
+constexpr int kNT = 2;                        // 32-column MFMA tiles per wave
+constexpr int kBM = 32 * kWavesM;             // 128
+constexpr int kBN = 32 * kNT * (kThreads / 64 / kWavesM);   // 128
+constexpr int kSB = 4;                        // 16-element blocks per stage
+constexpr int kSBLog = 2;
 constexpr int kRowBytes = kSB * 16 + 8;       // FP8 bytes per LDS row (+8 breaks bank aliasing)
-constexpr int kAItems = kBM * kSB / kThreads; // (row, block) items per thread: 4
-constexpr int kBItems = kBN * kSB / kThreads; // 2
+constexpr int kAItems = kBM * kSB / kThreads; // (row, block) items per thread: 1
+constexpr int kBItems = kBN * kSB / kThreads; // 1
+static_assert(kAItems * kThreads == kBM * kSB && kBItems * kThreads == kBN * kSB, "staging");
+static_assert((1 << kSBLog) == kSB, "kSBLog");
 constexpr int kMaxGemmGroups = 1024;
 constexpr int kXcds = 8;
 
@@ -108,7 +118,7 @@ struct Gemm {
 #pragma unroll
     for (int j = 0; j < kAItems; ++j) {
       const int i = tid + kThreads * j;
-      const int row = i >> 3, blk = i & 7;
+      const int row = i >> kSBLog, blk = i & (kSB - 1);
       const bool ok = kb + blk < job.kb1;
       const int oq = ok ? (int)(row * (g.kpad / 2) + (kb + blk) * 8) : 0x7FFFFFF8;
       const int os = ok ? (int)((row * kblocks + kb + blk) * 4) : 0x7FFFFFF8;
@@ -119,7 +129,7 @@ struct Gemm {
 #pragma unroll
     for (int j = 0; j < kBItems; ++j) {
       const int i = tid + kThreads * j;
-      const int row = i >> 3, blk = i & 7;
+      const int row = i >> kSBLog, blk = i & (kSB - 1);
       const bool ok = kb + blk < job.kb1;
       const int oq = ok ? (int)(row * (g.kpad / 2) + (kb + blk) * 8) : 0x7FFFFFF8;
       const int os = ok ? (int)((row * kblocks + kb + blk) * 4) : 0x7FFFFFF8;
@@ -134,7 +144,7 @@ struct Gemm {
 #pragma unroll
     for (int j = 0; j < kAItems; ++j) {
       const int i = tid + kThreads * j;
-      const int row = i >> 3, blk = i & 7;
+      const int row = i >> kSBLog, blk = i & (kSB - 1);
       uint2 *dst = reinterpret_cast<uint2 *>(s.a + row * kRowBytes + blk * 16);
       dst[0] = nib8_to_fp8<GRID>(r.aq[j].x);
       dst[1] = nib8_to_fp8<GRID>(r.aq[j].y);
@@ -143,7 +153,7 @@ struct Gemm {
 #pragma unroll
     for (int j = 0; j < kBItems; ++j) {
       const int i = tid + kThreads * j;
-      const int row = i >> 3, blk = i & 7;
+      const int row = i >> kSBLog, blk = i & (kSB - 1);
       uint2 *dst = reinterpret_cast<uint2 *>(s.b + row * kRowBytes + blk * 16);
       dst[0] = nib8_to_fp8<GRID>(r.bq[j].x);
       dst[1] = nib8_to_fp8<GRID>(r.bq[j].y);
@@ -151,25 +161,26 @@ struct Gemm {
     }
   }
 
-  // One stage: 8 blocks x (4 MFMA + 64 scale products + 64 FMAs) per wave.
-  __device__ __forceinline__ static void compute(const Stage &s, floatx16 (&acc)[4]) {
+  // One stage: kSB blocks x (2 MFMA + 32 scale products + 32 FMAs) per wave.
+  __device__ __forceinline__ static void compute(const Stage &s, floatx16 (&acc)[kNT]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int wm = wave % kWavesM, wn = wave / kWavesM;
     const int l32 = lane & 31;
     const int half = lane >> 5;
     floatx16 zero;
 #pragma unroll
     for (int r = 0; r < 16; ++r) zero[r] = 0.0f;
-    const uint8_t *pa = s.a + (wave * 32 + l32) * kRowBytes + 8 * half;
-    const uint8_t *pb = s.b + l32 * kRowBytes + 8 * half;
-    const float *psa = s.sa + wave * 32 + 4 * half;
-    const float *psb = s.sb + l32;
+    const uint8_t *pa = s.a + (wm * 32 + l32) * kRowBytes + 8 * half;
+    const uint8_t *pb = s.b + (wn * 32 * kNT + l32) * kRowBytes + 8 * half;
+    const float *psa = s.sa + wm * 32 + 4 * half;
+    const float *psb = s.sb + wn * 32 * kNT + l32;
 #pragma unroll 1
     for (int b = 0; b < kSB; ++b) {
       const long af = *reinterpret_cast<const long *>(pa + b * 16);
-      floatx16 p[4];
+      floatx16 p[kNT];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         const long bf = *reinterpret_cast<const long *>(pb + nt * 32 * kRowBytes + b * 16);
         p[nt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af, bf, zero, 0, 0, 0);
       }
@@ -183,7 +194,7 @@ struct Gemm {
         sa[4 * j + 3] = v.w;
       }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         const float sb = psb[b * kBN + nt * 32];
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nt][r] = fmaf(sa[r] * sb, p[nt][r], acc[nt][r]);
@@ -192,9 +203,9 @@ struct Gemm {
   }
 
   __device__ void run(Stage *stages) {
-    floatx16 acc[4];
+    floatx16 acc[kNT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
@@ -215,15 +226,26 @@ struct Gemm {
     constexpr float inv_g2 = (GRID == kGridUniform) ? (1.0f / 49.0f) : (1.0f / 144.0f);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int wm = wave % kWavesM, wn = wave / kWavesM;
     const int l32 = lane & 31;
     const int half = lane >> 5;
+    // Row offsets r -> 8*(r/4) + (r%4) are wave-uniform, so the per-lane part
+    // is one pointer and one remaining-rows count.  ldc goes through an empty
+    // asm so that the sixteen row offsets are formed here, after the K loop,
+    // instead of being hoisted and held in registers across it.
+    int64_t ldc = g.ldc;
+    asm volatile("" : "+s"(ldc));
+    const int m0 = wm * 32 + 4 * half;
+    const int n0 = wn * kNT * 32 + l32;
+    const int mrem = (int)job.a_rows - m0;
+    const int nrem = (int)job.b_rows - n0;
+    float *cl = job.c + m0 * ldc + n0;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = nt * 32 + l32;
+    for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m < job.a_rows && n < job.b_rows) job.c[(int64_t)m * g.ldc + n] = acc[nt][r] * inv_g2;
+        const int dm = 8 * (r >> 2) + (r & 3);
+        if (nt * 32 < nrem && dm < mrem) cl[dm * ldc + nt * 32] = acc[nt][r] * inv_g2;
       }
     }
   }
@@ -292,16 +314,25 @@ __device__ void load_gemm_groups(const GemmArgs &g, int64_t *s_off, int64_t *s_p
   }
 }
 
-// XCD-major tile order: workgroups are dispatched to the 8 XCDs round robin,
-// so workgroup b runs on XCD b % 8; XCD x walks the contiguous tile range
-// [x * per, (x + 1) * per).
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t span) {
-  const int64_t per = span / kXcds;
-  return (b % kXcds) * per + b / kXcds;
+// Banded order of a tiles_m x tiles_n tile grid: bands of kBand tile rows,
+// column-major inside a band.  The 64 tiles an XCD runs at once (32 CUs x 2
+// workgroups) then span 8 A row panels and 8 B column panels, which fit its
+// 4 MB L2 together, and the A panels stay resident while the band sweeps N.
+constexpr int kBand = 8;
+__device__ __forceinline__ void band_tile(int64_t local, int64_t tiles_m, int64_t tiles_n,
+                                          int64_t &tm, int64_t &tn) {
+  const int64_t band = local / (kBand * tiles_n);
+  const int64_t r = local - band * kBand * tiles_n;
+  const int64_t left = tiles_m - band * kBand;
+  const int rows = (int)(left < kBand ? left : kBand);
+  const int64_t q = r / rows;
+  tn = q;
+  tm = band * kBand + (r - q * rows);
 }
 
 template <int GRID, int MODE>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(4, 4))) void gemm_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Stage *stages = reinterpret_cast<Stage *>(smem);
   int64_t *s_off = reinterpret_cast<int64_t *>(smem + 2 * sizeof(Stage));
@@ -318,20 +349,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   if (MODE == 0) total = tiles_m * tiles_n;
   else if (MODE == 1) total = s_pre[g.n_groups];
   else total = (int64_t)g.n_groups * tiles_m * tiles_n;
-  // Iteration space: a multiple of both the grid and the XCD count, >= total.
+  // Dense and M-grouped tiles all cost the same K, so each XCD takes a
+  // contiguous range of the tile order (L2 reuse of A and B panels): the
+  // workgroups of XCD x (every kXcds-th one, as the dispatcher deals them out
+  // round robin) stride through [x * per, (x + 1) * per).  K-grouped tiles
+  // differ in cost by group, so they go round robin, heaviest group first.
   const int64_t slots = (int64_t)gridDim.x;
-  const int64_t quantum = slots % kXcds == 0 ? slots : slots * kXcds;
-  const int64_t span = (total + quantum - 1) / quantum * quantum;
+  const int64_t lanes = slots < kXcds ? slots : kXcds;
+  const int64_t xcd = (MODE == 2) ? 0 : (int64_t)blockIdx.x % lanes;
+  const int64_t per = (MODE == 2) ? total : (total + lanes - 1) / lanes;
+  const int64_t t_end = min(xcd * per + per, total);
+  const int64_t t_step = (MODE == 2) ? slots : (slots - xcd + lanes - 1) / lanes;
+  const int64_t t_first = (MODE == 2) ? (int64_t)blockIdx.x
+                                      : xcd * per + (int64_t)blockIdx.x / lanes;
 
-  for (int64_t b = blockIdx.x; b < span; b += slots) {
-    // Dense and M-grouped tiles all cost the same K, so each XCD takes a
-    // contiguous range (L2 reuse of A row panels); K-grouped tiles differ in
-    // cost by group, so they go round robin, heaviest group first.
-    const int64_t t = (MODE == 2) ? b : xcd_tile(b, span);
-    if (t >= total) continue;
+  for (int64_t t = t_first; t < t_end; t += t_step) {
     TileJob job;
     if (MODE == 0) {
-      const int64_t tm = t / tiles_n, tn = t - tm * tiles_n;
+      int64_t tm, tn;
+      band_tile(t, tiles_m, tiles_n, tm, tn);
       job.a_row0 = tm * kBM;
       job.a_rows = min((int64_t)kBM, g.M - job.a_row0);
       job.b_row0 = tn * kBN;
@@ -347,7 +383,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       }
       const int e = lo;
       const int64_t local = t - s_pre[e];
-      const int64_t tm = local / tiles_n, tn = local - tm * tiles_n;
+      int64_t tm, tn;
+      band_tile(local, (s_pre[e + 1] - s_pre[e]) / tiles_n, tiles_n, tm, tn);
       job.a_row0 = s_off[e] + tm * kBM;
       job.a_rows = min((int64_t)kBM, s_off[e + 1] - job.a_row0);
       job.b_row0 = (int64_t)e * g.N + tn * kBN;
