@@ -1,15 +1,18 @@
 """Throughput of the UFP4 hot path on one MI355X.
 
 A step is one pass of the whole path over the dense 1.5B-model linear layer
-(tokens 8192, hidden 2048, FFN 8192): the six quantizations of the UFP4
+(tokens 8192, hidden 2048, FFN 8192): the six quantized operands of the UFP4
 recipe (X and W along H for FPROP; dY along F with stochastic rounding and W
 along F for DGRAD; dY and X along the tokens for WGRAD, dY with stochastic
-rounding) and the three block-scaled 4-bit GEMMs.  Inputs are synthetic
-(seeded, see uniform_grid_fp4_amd/workloads.py) and resident in HBM before
-the timed region.
+rounding) and the three block-scaled 4-bit GEMMs.  By default the operands
+come from three dual-axis quantizations (one read of X, W and dY each, both
+of the tensor's operands out; bit-identical to the six single-axis calls,
+which `--quantizer single` runs instead).  Inputs are synthetic (seeded, see
+uniform_grid_fp4_amd/workloads.py) and resident in HBM before the timed
+region.
 
 Prints one JSON line.  `value` is the whole step's throughput in GEMM
-TFLOP/s (3 x 2*T*H*F FLOP per step over the wall time of the step, the six
+TFLOP/s (3 x 2*T*H*F FLOP per step over the wall time of the step, the
 quantizations included); the quantizer and GEMM kernels are also reported on
 their own, timed with HIP events on the stream they run on.
 """
@@ -36,6 +39,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA
 VALU_LANE_OPS = 256 * 4 * 32 * 2.4e9
 GEMM_ALU_PEAK_TFLOPS = VALU_LANE_OPS * 16.0 / 2.0 * 2.0 / 1e12
 BYTES_PER_QUANT_ELEM = 2.0 + 0.5 + 0.25
+BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 
 # HBM bytes per GEMM launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE
 # counters (averaged over the FPROP, DGRAD and WGRAD launches of one step),
@@ -74,6 +78,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--quantizer", default="dual", choices=["single", "dual"],
+                    help="single: six single-axis quantizations per step; dual: three dual-axis "
+                         "quantizations (one read of X, W and dY each, both operands out)")
     ap.add_argument("--workload", default="dense-1.5b",
                     choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b", "copy"],
                     help="dense-1.5b: the timed step (default); quant-sweep: the 2^28-element "
@@ -87,8 +94,10 @@ def parse():
 class Step:
     """Buffers and calls of one pass of the hot path."""
 
-    def __init__(self, L, U, torch):
+    def __init__(self, L, U, torch, dual=False):
         self.L, self.U, self.torch = L, U, torch
+        self.dual = dual
+        self.quant_names = self.QUANT_DUAL if dual else self.QUANT
         T, H, F = L.x.shape[0], L.hidden, L.ffn
         self.T, self.H, self.F = T, H, F
         self.mf, self.md, self.mw = L.masks
@@ -111,6 +120,19 @@ class Step:
         self.q[name] = q
         return q
 
+    def quant2(self, name, x, rowwise, colwise, rnd, ev, **kw):
+        """Both operands of x from one read (dual-axis quantizer)."""
+        U = self.U
+        if ev is not None:
+            ev[name][0].record()
+        prev = self.q.get(name, (None, None))
+        q = U.ufp4_rht_quantize_dual(x, rowwise, colwise, grid=U.GRID_UNIFORM, rnd=rnd,
+                                     seed=self.seed, out_rows=prev[0], out_cols=prev[1], **kw)
+        if ev is not None:
+            ev[name][1].record()
+        self.q[name] = q
+        return q
+
     def gemm(self, name, fn, a, b, out, ev):
         if ev is not None:
             ev[name][0].record()
@@ -121,6 +143,17 @@ class Step:
     def run(self, ev):
         U, L = self.U, self.L
         C, R = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS
+        if self.dual:
+            xq, xtq = self.quant2("q_x_dual", L.x, (True, self.mf, 0), (True, self.mw, 0),
+                                  U.ROUND_RTNE, ev)
+            wq, wtq = self.quant2("q_w_dual", L.w, (True, self.mf, 0), (True, self.md, 0),
+                                  U.ROUND_RTNE, ev)
+            self.gemm("fprop", U.ufp4_gemm_fprop, xq, wq, self.y, ev)
+            dyq, dytq = self.quant2("q_dy_dual", L.dy, (True, self.md, 0), (True, self.mw, 1),
+                                    U.ROUND_SR, ev)
+            self.gemm("dgrad", U.ufp4_gemm_dgrad, dyq, wtq, self.dx, ev)
+            self.gemm("wgrad", U.ufp4_gemm_wgrad, dytq, xtq, self.dw, ev)
+            return
         xq = self.quant("q_x_fprop", L.x, C, self.mf, U.ROUND_RTNE, 0, ev)
         wq = self.quant("q_w_fprop", L.w, C, self.mf, U.ROUND_RTNE, 0, ev)
         self.gemm("fprop", U.ufp4_gemm_fprop, xq, wq, self.y, ev)
@@ -132,12 +165,21 @@ class Step:
         self.gemm("wgrad", U.ufp4_gemm_wgrad, dytq, xtq, self.dw, ev)
 
     QUANT = ("q_x_fprop", "q_w_fprop", "q_dy_dgrad", "q_wt_dgrad", "q_dyt_wgrad", "q_xt_wgrad")
+    QUANT_DUAL = ("q_x_dual", "q_w_dual", "q_dy_dual")
     GEMMS = ("fprop", "dgrad", "wgrad")
 
     def quant_elems(self):
         T, H, F = self.T, self.H, self.F
         return {"q_x_fprop": T * H, "q_w_fprop": F * H, "q_dy_dgrad": T * F,
-                "q_wt_dgrad": F * H, "q_dyt_wgrad": T * F, "q_xt_wgrad": T * H}
+                "q_wt_dgrad": F * H, "q_dyt_wgrad": T * F, "q_xt_wgrad": T * H,
+                "q_x_dual": T * H, "q_w_dual": F * H, "q_dy_dual": T * F}
+
+    def quant_bytes(self):
+        """Algorithmic bytes of each quantizer call of the step: 2 B read and
+        0.75 B written per element and output (two outputs for a dual call)."""
+        el = self.quant_elems()
+        return {n: el[n] * (BYTES_PER_DUAL_ELEM if n.endswith("_dual") else BYTES_PER_QUANT_ELEM)
+                for n in self.quant_names}
 
     def gemm_flops(self):
         return 2.0 * self.T * self.H * self.F
@@ -203,11 +245,11 @@ class MoeStep(Step):
     dY^T and X^T column-wise with per-expert padding, then the three grouped
     GEMMs."""
 
-    def __init__(self, L, U, torch):
+    def __init__(self, L, U, torch, dual=False):
         self.offd = torch.as_tensor(L.offsets, device=L.x.device)
         self.E = L.experts
         self.tokens = int(L.offsets[-1])
-        super().__init__(L, U, torch)
+        super().__init__(L, U, torch, dual)
 
     def quant(self, name, x, axis, mask, rnd, sid, ev, **kw):
         U = self.U
@@ -236,6 +278,17 @@ class MoeStep(Step):
             self.y = self.torch.empty((T, F), dtype=self.torch.float32, device=dev)
             self.dx = self.torch.empty((T, H), dtype=self.torch.float32, device=dev)
             self.dwg = self.torch.empty((E, F, H), dtype=self.torch.float32, device=dev)
+        if self.dual:
+            xq, xtq = self.quant2("q_x_dual", L.x, (True, self.mf, 0), (True, self.mw, 0),
+                                  U.ROUND_RTNE, ev, group_offsets=self.offd)
+            wq, wtq = self.quant2("q_w_dual", L.w, (True, self.mf, 0), (True, self.md, 0),
+                                  U.ROUND_RTNE, ev, col_axis=S, n_groups=self.E)
+            self.gemm("fprop", U.FPROP, xq, wq, self.y, ev)
+            dyq, dytq = self.quant2("q_dy_dual", L.dy, (True, self.md, 0), (True, self.mw, 1),
+                                    U.ROUND_SR, ev, group_offsets=self.offd)
+            self.gemm("dgrad", U.DGRAD, dyq, wtq, self.dx, ev)
+            self.gemm("wgrad", U.WGRAD, dytq, xtq, self.dwg, ev)
+            return
         xq = self.quant("q_x_fprop", L.x, C, self.mf, U.ROUND_RTNE, 0, ev)
         wq = self.quant("q_w_fprop", L.w, C, self.mf, U.ROUND_RTNE, 0, ev)
         self.gemm("fprop", U.FPROP, xq, wq, self.y, ev)
@@ -251,7 +304,8 @@ class MoeStep(Step):
     def quant_elems(self):
         T, H, F, E = self.tokens, self.H, self.F, self.E
         return {"q_x_fprop": T * H, "q_w_fprop": E * F * H, "q_dy_dgrad": T * F,
-                "q_wt_dgrad": E * F * H, "q_dyt_wgrad": T * F, "q_xt_wgrad": T * H}
+                "q_wt_dgrad": E * F * H, "q_dyt_wgrad": T * F, "q_xt_wgrad": T * H,
+                "q_x_dual": T * H, "q_w_dual": E * F * H, "q_dy_dual": T * F}
 
     def gemm_flops(self):
         return 2.0 * self.tokens * self.H * self.F
@@ -352,19 +406,19 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "moe-7.9b":
         L = W.moe_7p9b(dev)
-        st = MoeStep(L, U, torch)
+        st = MoeStep(L, U, torch, args.quantizer == "dual")
     elif args.workload == "moe-124b":
         L = W.moe_124b(dev)
-        st = MoeStep(L, U, torch)
+        st = MoeStep(L, U, torch, args.quantizer == "dual")
     else:
         L = W.dense_1p5b(dev)
-        st = Step(L, U, torch)
+        st = Step(L, U, torch, args.quantizer == "dual")
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         st.run(None)
     torch.cuda.synchronize()
 
-    names = Step.QUANT + Step.GEMMS
+    names = st.quant_names + Step.GEMMS
     evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for n in names} for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -376,9 +430,8 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     dur = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}
-    qel = st.quant_elems()
-    q_ms = sum(dur[n] for n in Step.QUANT)
-    q_bytes = sum(qel.values()) * BYTES_PER_QUANT_ELEM
+    q_ms = sum(dur[n] for n in st.quant_names)
+    q_bytes = sum(st.quant_bytes().values())
     g_ms = sum(dur[n] for n in Step.GEMMS)
     g_flop = 3 * st.gemm_flops()
     gemm_avg_ms = g_ms / 3
@@ -405,7 +458,8 @@ def main():
         "quantize": {"gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                      "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "ms_per_step": round(q_ms, 4),
-                     "per_call_ms": {n: round(dur[n], 4) for n in Step.QUANT},
+                     "per_call_ms": {n: round(dur[n], 4) for n in st.quant_names},
+                     "kernels": "dual-axis" if st.dual else "single-axis",
                      "bytes_per_step": q_bytes},
         "gemm": {"tflops": round(gemm_tflops, 2),
                  "frac_fp8_mfma_peak": round(gemm_tflops / FP8_MFMA_PEAK_TFLOPS, 4),

@@ -145,6 +145,44 @@ ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_
                               int32_t grid, int32_t rnd, uint64_t seed, uint32_t stream_id,
                               ufp4_qtensor *out, hipStream_t stream);
 
+/* The options that differ between the two outputs of a dual-axis
+ * quantization (host struct read during the call). */
+typedef struct {
+  int32_t rht;        /* 1: apply the 16-point RHT with sign_mask            */
+  uint32_t sign_mask; /* bits 0..15, as in ufp4_rht_quantize                 */
+  uint32_t stream_id; /* SR stream of this output (ignored for RTNE)         */
+  int32_t reserved;   /* must be 0                                           */
+} ufp4_quant_side;
+
+/* ufp4_rht_quantize_dual -- both operands of one tensor from a single read of
+ * it.  Each training tensor feeds two GEMMs that contract it along different
+ * dimensions (X: FPROP along H, WGRAD along T; W: FPROP along H, DGRAD along
+ * F; dY: DGRAD along F, WGRAD along T -- paperlayer.ai section 2 "Random
+ * Hadamard transforms"), so it is quantized once per axis; the pages' fusion
+ * argument for the RHT (the transform rides along with the quantizer's memory
+ * traffic) applies to the second axis too.
+ *   out_rows: bit-identical to ufp4_rht_quantize(x, ALONG_COLS, NULL, 0,
+ *             rowwise->rht, rowwise->sign_mask, grid, rnd, seed,
+ *             rowwise->stream_id, out_rows).
+ *   out_cols: bit-identical to ufp4_rht_quantize(x, col_axis,
+ *             d_group_offsets, n_groups, colwise->rht, colwise->sign_mask,
+ *             grid, rnd, seed, colwise->stream_id, out_cols).
+ * col_axis: UFP4_BLOCKS_ALONG_ROWS (optionally grouped by d_group_offsets /
+ *   n_groups, as in ufp4_rht_quantize) or UFP4_BLOCKS_ALONG_ROWS_STACKED
+ *   (d_group_offsets NULL, n_groups stacks).
+ * grid, rnd and seed are shared by both outputs.  The two outputs must not
+ * share buffers.  Traffic: 2 B read + 2 x 0.75 B written per element, against
+ * 2 x 2.75 B for the two single-axis calls.
+ * Returns UFP4_OK, INVALID_ARG (null pointer, bad enum or axis, reserved != 0,
+ *   shared output buffers, misalignment), SHAPE (either output's rows/kpad
+ *   not what its single-axis call would require), HIP. */
+ufp4_status ufp4_rht_quantize_dual(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols,
+                                   int64_t ld, int32_t col_axis, const int64_t *d_group_offsets,
+                                   int32_t n_groups, int32_t grid, int32_t rnd, uint64_t seed,
+                                   const ufp4_quant_side *rowwise, const ufp4_quant_side *colwise,
+                                   ufp4_qtensor *out_rows, ufp4_qtensor *out_cols,
+                                   hipStream_t stream);
+
 /* ufp4_dequantize -- out[r, k] for k < kpad, FP32 row-major with stride
  * ld_out >= kpad:  (float)((double)(sign*L[idx]) * (double)s / g)  (the
  * dequantized value of paperlayer.ai section 2 "Blockwise quantization").

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     decl = declared_functions()
-    assert len(decl) == 8, decl
+    assert len(decl) == 9, decl
     assert sorted(U.EXPORTS) == decl
     L = U.lib()
     for name in decl:
@@ -119,3 +119,39 @@ def test_dequantize_validation():
     assert L.ufp4_dequantize(ctypes.byref(ok), 0, FAKE, 16, None) == -2
     assert L.ufp4_dequantize(ctypes.byref(fake_desc(rht=0)), 1, FAKE, 32, None) == -1
     assert L.ufp4_dequantize(None, 0, FAKE, 32, None) == -1
+
+
+def dual(**kw):
+    a = dict(x=FAKE, n_rows=32, n_cols=48, ld=48, axis=1, goff=None, ng=0, grid=0, rnd=0, seed=1,
+             rs=U.QuantSide(1, 0x1234, 0, 0), cs=U.QuantSide(1, 0x4321, 1, 0),
+             outr=fake_desc(rows=32, kpad=48), outc=fake_desc(rows=48, kpad=32, codes=0x3000,
+                                                              scales=0x4000))
+    a.update(kw)
+    return U.lib().ufp4_rht_quantize_dual(a["x"], a["n_rows"], a["n_cols"], a["ld"], a["axis"],
+                                          a["goff"], a["ng"], a["grid"], a["rnd"], a["seed"],
+                                          None if a["rs"] is None else ctypes.byref(a["rs"]),
+                                          None if a["cs"] is None else ctypes.byref(a["cs"]),
+                                          None if a["outr"] is None else ctypes.byref(a["outr"]),
+                                          None if a["outc"] is None else ctypes.byref(a["outc"]),
+                                          None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), -1), (dict(rs=None), -1), (dict(cs=None), -1), (dict(outr=None), -1),
+    (dict(outc=None), -1),
+    (dict(axis=0), -1), (dict(axis=3), -1),            # the second output is column-wise
+    (dict(rs=U.QuantSide(1, 0, 0, 7)), -1),           # reserved
+    (dict(cs=U.QuantSide(2, 0, 0, 0)), -1),           # rht not 0/1
+    (dict(rs=U.QuantSide(1, 0x10000, 0, 0)), -1),     # mask > 16 bits
+    (dict(grid=2), -1), (dict(rnd=5), -1),
+    (dict(outc=fake_desc(rows=48, kpad=32)), -1),     # shares the row-wise buffers
+    (dict(outr=fake_desc(rows=32, kpad=32)), -2),     # row-wise kpad must be 48
+    (dict(outc=fake_desc(rows=32, kpad=32, codes=0x3000, scales=0x4000)), -2),  # rows = n_cols
+    (dict(axis=1, goff=FAKE, ng=2, outc=fake_desc(rows=48, kpad=32, codes=0x3000,
+                                                  scales=0x4000)), -2),   # >= roundup16(62)
+    (dict(axis=2, ng=3), -2),                          # stacks must divide n_rows
+    (dict(axis=2, goff=FAKE, ng=2), -1),
+    (dict(n_rows=0), -2), (dict(ld=40), -2),
+])
+def test_dual_quantize_rejects(kw, expect):
+    assert dual(**kw) == expect

@@ -165,3 +165,35 @@ def test_moe_124b_layer_one_gpu_share():
     print("[fullsize] MoE 124B expert layer, one GPU's share", flush=True)
     run_moe(W.moe_124b(DEV), 16, 4, 6)
     torch.cuda.empty_cache()
+
+
+def test_dense_1p5b_dual_quantizer():
+    """The dual-axis quantizer at the bench's full size and options: sampled
+    rows of every output equal the oracle, and whole outputs equal the
+    single-axis calls."""
+    L = W.dense_1p5b(DEV)
+    mf, md, mw = L.masks
+    T, H, F = L.x.shape[0], L.hidden, L.ffn
+    print("[fullsize] dense 1.5B layer, dual-axis quantizer", flush=True)
+    C, R = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS
+    xq, xtq = U.ufp4_rht_quantize_dual(L.x, (True, mf, 0), (True, mw, 0), seed=SEED)
+    wq, wtq = U.ufp4_rht_quantize_dual(L.w, (True, mf, 0), (True, md, 0), seed=SEED)
+    dyq, dytq = U.ufp4_rht_quantize_dual(L.dy, (True, md, 0), (True, mw, 1), rnd=U.ROUND_SR,
+                                         seed=SEED)
+    torch.cuda.synchronize()
+    check_rows_quant(xq, L.x, C, mf, 0, 0, sample(T, 32, 31), what="X row-wise")
+    check_rows_quant(xtq, L.x, R, mw, 0, 0, sample(H, 16, 32), what="X column-wise")
+    check_rows_quant(wq, L.w, C, mf, 0, 0, sample(F, 32, 33), what="W row-wise")
+    check_rows_quant(wtq, L.w, R, md, 0, 0, sample(H, 16, 34), what="W column-wise")
+    check_rows_quant(dyq, L.dy, C, md, 1, 0, sample(T, 32, 35), what="dY row-wise")
+    check_rows_quant(dytq, L.dy, R, mw, 1, 1, sample(F, 16, 36), what="dY column-wise")
+    singles = [
+        (xq, U.ufp4_rht_quantize(L.x, C, True, mf, seed=SEED)),
+        (xtq, U.ufp4_rht_quantize(L.x, R, True, mw, seed=SEED)),
+        (wq, U.ufp4_rht_quantize(L.w, C, True, mf, seed=SEED)),
+        (wtq, U.ufp4_rht_quantize(L.w, R, True, md, seed=SEED)),
+        (dyq, U.ufp4_rht_quantize(L.dy, C, True, md, rnd=U.ROUND_SR, seed=SEED, stream_id=0)),
+        (dytq, U.ufp4_rht_quantize(L.dy, R, True, mw, rnd=U.ROUND_SR, seed=SEED, stream_id=1)),
+    ]
+    for d, s in singles:
+        assert torch.equal(d.codes, s.codes) and torch.equal(d.scales, s.scales)

@@ -58,15 +58,12 @@ ufp4_status dense_gemm(const ufp4_qtensor *a, const ufp4_qtensor *b, float *c, i
   return launch_gemm(g, stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
-                              int32_t axis, const int64_t *d_group_offsets, int32_t n_groups,
-                              int32_t rht, uint32_t sign_mask, int32_t grid, int32_t rnd,
-                              uint64_t seed, uint32_t stream_id, ufp4_qtensor *out,
-                              hipStream_t stream) {
+// Every check of one quantization call (shared by the single and the
+// dual-axis entry points); nothing is launched unless it passes.
+ufp4_status check_quant(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
+                        int32_t axis, const int64_t *d_group_offsets, int32_t n_groups,
+                        int32_t rht, uint32_t sign_mask, int32_t grid, int32_t rnd,
+                        const ufp4_qtensor *out) {
   if (x_bf16 == nullptr || out == nullptr || out->codes == nullptr || out->scales == nullptr)
     return UFP4_ERR_INVALID_ARG;
   if (!aligned16(out->codes) || !aligned16(out->scales) || out->reserved != 0)
@@ -106,7 +103,30 @@ ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_
       return UFP4_ERR_SHAPE;
   }
   if (out->rows != rows) return UFP4_ERR_SHAPE;
+  return UFP4_OK;
+}
 
+void fill_quant_desc(ufp4_qtensor *out, int64_t n_rows, int64_t n_cols, int32_t axis,
+                     int32_t n_groups, int32_t rht, uint32_t sign_mask, int32_t grid) {
+  out->k = (axis == UFP4_BLOCKS_ALONG_COLS) ? n_cols
+           : (axis == UFP4_BLOCKS_ALONG_ROWS_STACKED) ? n_rows / n_groups : n_rows;
+  out->grid = grid;
+  out->rht = rht;
+  out->sign_mask = rht ? sign_mask : 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
+                              int32_t axis, const int64_t *d_group_offsets, int32_t n_groups,
+                              int32_t rht, uint32_t sign_mask, int32_t grid, int32_t rnd,
+                              uint64_t seed, uint32_t stream_id, ufp4_qtensor *out,
+                              hipStream_t stream) {
+  ufp4_status st = check_quant(x_bf16, n_rows, n_cols, ld, axis, d_group_offsets, n_groups, rht,
+                               sign_mask, grid, rnd, out);
+  if (st != UFP4_OK) return st;
   QuantArgs a{};
   a.x = x_bf16;
   a.n_rows = n_rows;
@@ -126,11 +146,58 @@ ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_
   a.codes = out->codes;
   a.scales = out->scales;
   if (launch_quantize(a, stream) != hipSuccess) return UFP4_ERR_HIP;
-  out->k = (axis == UFP4_BLOCKS_ALONG_COLS) ? n_cols
-           : (axis == UFP4_BLOCKS_ALONG_ROWS_STACKED) ? n_rows / n_groups : n_rows;
-  out->grid = grid;
-  out->rht = rht;
-  out->sign_mask = rht ? sign_mask : 0u;
+  fill_quant_desc(out, n_rows, n_cols, axis, n_groups, rht, sign_mask, grid);
+  return UFP4_OK;
+}
+
+ufp4_status ufp4_rht_quantize_dual(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols,
+                                   int64_t ld, int32_t col_axis, const int64_t *d_group_offsets,
+                                   int32_t n_groups, int32_t grid, int32_t rnd, uint64_t seed,
+                                   const ufp4_quant_side *rowwise, const ufp4_quant_side *colwise,
+                                   ufp4_qtensor *out_rows, ufp4_qtensor *out_cols,
+                                   hipStream_t stream) {
+  if (rowwise == nullptr || colwise == nullptr || out_rows == nullptr || out_cols == nullptr)
+    return UFP4_ERR_INVALID_ARG;
+  if (rowwise->reserved != 0 || colwise->reserved != 0) return UFP4_ERR_INVALID_ARG;
+  if (col_axis != UFP4_BLOCKS_ALONG_ROWS && col_axis != UFP4_BLOCKS_ALONG_ROWS_STACKED)
+    return UFP4_ERR_INVALID_ARG;
+  if (out_rows->codes == out_cols->codes || out_rows->scales == out_cols->scales)
+    return UFP4_ERR_INVALID_ARG;
+  ufp4_status st = check_quant(x_bf16, n_rows, n_cols, ld, UFP4_BLOCKS_ALONG_COLS, nullptr, 0,
+                               rowwise->rht, rowwise->sign_mask, grid, rnd, out_rows);
+  if (st != UFP4_OK) return st;
+  st = check_quant(x_bf16, n_rows, n_cols, ld, col_axis, d_group_offsets, n_groups, colwise->rht,
+                   colwise->sign_mask, grid, rnd, out_cols);
+  if (st != UFP4_OK) return st;
+  DualArgs a{};
+  a.x = x_bf16;
+  a.n_rows = n_rows;
+  a.n_cols = n_cols;
+  a.ld = ld;
+  a.col_axis = col_axis;
+  a.goff = d_group_offsets;
+  a.n_groups = n_groups;
+  a.grid = grid;
+  a.rnd = rnd;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.rht_r = rowwise->rht;
+  a.mask_r = rowwise->rht ? rowwise->sign_mask : 0u;
+  a.sid_r = rowwise->stream_id;
+  a.kpad_r = out_rows->kpad;
+  a.codes_r = out_rows->codes;
+  a.scales_r = out_rows->scales;
+  a.rht_c = colwise->rht;
+  a.mask_c = colwise->rht ? colwise->sign_mask : 0u;
+  a.sid_c = colwise->stream_id;
+  a.kpad_c = out_cols->kpad;
+  a.codes_c = out_cols->codes;
+  a.scales_c = out_cols->scales;
+  if (launch_quantize_dual(a, stream) != hipSuccess) return UFP4_ERR_HIP;
+  fill_quant_desc(out_rows, n_rows, n_cols, UFP4_BLOCKS_ALONG_COLS, 0, rowwise->rht,
+                  rowwise->sign_mask, grid);
+  fill_quant_desc(out_cols, n_rows, n_cols, col_axis, n_groups, colwise->rht, colwise->sign_mask,
+                  grid);
   return UFP4_OK;
 }
 

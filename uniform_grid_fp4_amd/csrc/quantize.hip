@@ -368,6 +368,206 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Dual-axis: one read of x gives both operands of a tensor -- the row-wise
+// one (blocks along the contiguous dimension, as the row-wise kernels write
+// it) and the transposed column-wise one (as quant_cols_kernel, with the same
+// tiles, groups and stacking).  Each lane's two columns x 16 rows of the
+// current row-block also go to a per-wave LDS buffer; read back as 16 rows x
+// 8 blocks of 16 columns, they give the row-wise blocks: lane l takes row l/4
+// and blocks 2(l%4), 2(l%4)+1 of the tile's 128 columns.  Each output is
+// bit-identical to the single-axis call with the same options; the bf16 input
+// is read once instead of twice.
+// ---------------------------------------------------------------------------
+template <int GRID, int RND>
+__device__ __forceinline__ void quantize_block_rt(bool rht, float (&v)[16], uint64_t idx0,
+                                                  uint32_t seed_lo, uint32_t seed_hi,
+                                                  uint32_t stream_id, uint32_t &w0, uint32_t &w1,
+                                                  float &s) {
+  if (rht)
+    quantize_block<GRID, RND, true>(v, idx0, seed_lo, seed_hi, stream_id, w0, w1, s);
+  else
+    quantize_block<GRID, RND, false>(v, idx0, seed_lo, seed_hi, stream_id, w0, w1, s);
+}
+
+// 8 dwords (16 bf16 along the block) -> FP32 with the RHT signs of `mask`
+// (0 when the side has no RHT).
+__device__ __forceinline__ void unpack_block(const uint4 a0, const uint4 a1, uint32_t mask,
+                                             float (&v)[16]) {
+  const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = bf16_lo(w[i], sign_bit(mask, 2 * i));
+    v[2 * i + 1] = bf16_hi(w[i], sign_bit(mask, 2 * i + 1));
+  }
+}
+
+template <int GRID, int RND, bool VEC, bool GROUPED>
+__global__ __launch_bounds__(256) void quant_dual_kernel(const DualArgs a, int64_t n_rows,
+                                                         int64_t n_stack) {
+  constexpr int kTabs = GROUPED ? kMaxGroups + 1 : 1;
+  constexpr int kTrStride = 68;                     // dwords per staged row (64 + 4 pad)
+  __shared__ int64_t s_off[kTabs];
+  __shared__ int64_t s_poff[kTabs];
+  __shared__ int64_t s_scan[GROUPED ? 256 : 1];
+  __shared__ uint2 s_codes[kColTileCols][kColTileRows / 16 + 1];
+  __shared__ float s_scales[kColTileCols][kColTileRows / 16 + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t s_tr[4][16 * kTrStride];
+
+  const int64_t n_cols = a.n_cols, ld = a.ld, kpad = a.kpad_c;
+  int64_t padded_end;
+  if (GROUPED) {
+    load_group_tables(a.goff, a.n_groups, n_rows, s_off, s_poff, s_scan);
+    padded_end = s_poff[a.n_groups];
+  } else {
+    padded_end = (n_rows + 15) / 16 * 16;
+  }
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t kblocks = kpad / 16;
+  const int64_t kblocks_r = a.kpad_r / 16;
+  const bool pair_aligned = (a.kpad_r % 32) == 0;   // 16-byte code / 8-byte scale pairs
+  const int64_t n_ptiles = (kpad + kColTileRows - 1) / kColTileRows;
+  const int64_t n_ctiles = (n_cols + kColTileCols - 1) / kColTileCols;
+  const int64_t per_stack = n_ptiles * n_ctiles;
+  const int64_t total = per_stack * n_stack;
+  uint32_t *tr = s_tr[wave];
+  const int rr = lane >> 2, c2 = lane & 3;            // row-wise: row and block pair
+
+  auto block_rows = [&](int64_t p, int64_t &row0, int &valid) {
+    row0 = 0;
+    valid = 0;
+    if (p < kblocks && 16 * p < padded_end) {
+      if (GROUPED) {
+        const int e = find_group(s_poff, a.n_groups, 16 * p);
+        row0 = s_off[e] + (16 * p - s_poff[e]);
+        const int64_t left = s_off[e + 1] - row0;
+        valid = left >= 16 ? 16 : (int)(left > 0 ? left : 0);
+      } else {
+        row0 = 16 * p;
+        const int64_t left = n_rows - row0;
+        valid = left >= 16 ? 16 : (int)left;
+      }
+    }
+    row0 = uniform64(row0);
+    valid = __builtin_amdgcn_readfirstlane(valid);
+  };
+
+  for (int64_t tile_all = blockIdx.x; tile_all < total; tile_all += gridDim.x) {
+    const int64_t si = tile_all / per_stack;
+    const int64_t tile = tile_all - si * per_stack;
+    const int64_t pt = tile / n_ctiles;
+    const int64_t ct = tile - pt * n_ctiles;
+    const uint16_t *xs = a.x + si * n_rows * ld;
+    const int64_t out_row0 = si * n_cols;
+    const int64_t pb0 = pt * (kColTileRows / 16);
+    const int64_t col0 = ct * kColTileCols;
+    const int64_t col = col0 + 2 * lane;
+    const uint32_t keep = (col + 1 < n_cols) ? 0xFFFFFFFFu : (col < n_cols ? 0x0000FFFFu : 0u);
+    const int col2 = (int)(col * 2);
+    const int64_t kbr0 = col0 / 16 + 2 * c2;           // this lane's first row-wise block
+    uint32_t cur[16], nxt[16];
+    int64_t row0, nrow0;
+    int valid, nvalid;
+    block_rows(pb0 + wave, row0, valid);
+    load_col_block<VEC>(xs, ld, n_cols, row0, valid, col2, keep, cur);
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+      const int rb = wave + 4 * q;
+      const int64_t p = pb0 + rb;
+      if (q < 3) {
+        block_rows(p + 4, nrow0, nvalid);
+        load_col_block<VEC>(xs, ld, n_cols, nrow0, nvalid, col2, keep, nxt);
+      }
+      // stage the raw dwords for the row-wise side
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tr[j * kTrStride + lane] = cur[j];
+      __builtin_amdgcn_wave_barrier();
+      const uint4 *trr = reinterpret_cast<const uint4 *>(tr + rr * kTrStride + 16 * c2);
+      const uint4 r0 = trr[0], r1 = trr[1], r2 = trr[2], r3 = trr[3];
+      __builtin_amdgcn_wave_barrier();
+
+      // column-wise side (transposed output through LDS, as quant_cols_kernel)
+      {
+        float va[16], vb[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          va[j] = bf16_lo(cur[j], sign_bit(a.mask_c, j));
+          vb[j] = bf16_hi(cur[j], sign_bit(a.mask_c, j));
+        }
+        uint32_t a0, a1, b0, b1;
+        float sa, sb;
+        const uint64_t base_a = (uint64_t)(out_row0 + col) * (uint64_t)kpad + (uint64_t)p * 16u;
+        const uint64_t base_b = base_a + (uint64_t)kpad;
+        quantize_block_rt<GRID, RND>(a.rht_c, va, base_a, a.seed_lo, a.seed_hi, a.sid_c, a0, a1,
+                                     sa);
+        quantize_block_rt<GRID, RND>(a.rht_c, vb, base_b, a.seed_lo, a.seed_hi, a.sid_c, b0, b1,
+                                     sb);
+        s_codes[2 * lane][rb] = make_uint2(a0, a1);
+        s_codes[2 * lane + 1][rb] = make_uint2(b0, b1);
+        s_scales[2 * lane][rb] = sa;
+        s_scales[2 * lane + 1][rb] = sb;
+      }
+
+      // row-wise side: row row0 + rr, blocks kbr0 and kbr0 + 1
+      if (rr < valid && kbr0 < kblocks_r) {
+        const int64_t grow = si * n_rows + row0 + rr;
+        const bool two = kbr0 + 1 < kblocks_r;
+        float v[16];
+        uint32_t w0, w1, w2 = 0, w3 = 0;
+        float s0, s1 = 0.0f;
+        unpack_block(r0, r1, a.mask_r, v);
+        quantize_block_rt<GRID, RND>(a.rht_r, v, (uint64_t)(grow * a.kpad_r + kbr0 * 16),
+                                     a.seed_lo, a.seed_hi, a.sid_r, w0, w1, s0);
+        if (two) {
+          unpack_block(r2, r3, a.mask_r, v);
+          quantize_block_rt<GRID, RND>(a.rht_r, v, (uint64_t)(grow * a.kpad_r + kbr0 * 16 + 16),
+                                       a.seed_lo, a.seed_hi, a.sid_r, w2, w3, s1);
+        }
+        uint8_t *cq = a.codes_r + grow * (a.kpad_r / 2) + kbr0 * 8;
+        float *cs = a.scales_r + grow * kblocks_r + kbr0;
+        if (two && pair_aligned) {
+          *reinterpret_cast<uint4 *>(cq) = make_uint4(w0, w1, w2, w3);
+          *reinterpret_cast<float2 *>(cs) = make_float2(s0, s1);
+        } else {
+          *reinterpret_cast<uint2 *>(cq) = make_uint2(w0, w1);
+          cs[0] = s0;
+          if (two) {
+            *reinterpret_cast<uint2 *>(cq + 8) = make_uint2(w2, w3);
+            cs[1] = s1;
+          }
+        }
+      }
+      if (q < 3) {
+        row0 = nrow0;
+        valid = nvalid;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+      }
+    }
+    __syncthreads();
+    const int nb = (int)((kblocks - pb0) < 16 ? (kblocks - pb0) : 16);
+    const int blk = tid & 15;
+    const int c0 = tid >> 4;
+    uint8_t *dq = a.codes_c + (out_row0 + col0 + c0) * (kpad / 2) + (pb0 + blk) * 8;
+    float *ds = a.scales_c + (out_row0 + col0 + c0) * kblocks + pb0 + blk;
+    const int64_t step_q = 16 * (kpad / 2), step_s = 16 * kblocks;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int c = c0 + 16 * it;
+      if (col0 + c < n_cols && blk < nb) {
+        *reinterpret_cast<uint2 *>(dq) = s_codes[c][blk];
+        *ds = s_scales[c][blk];
+      }
+      dq += step_q;
+      ds += step_s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Dequantizer: one lane per block.  value = (float)((double)(sign*L) *
 // (double)s / g); with the inverse RHT the FP64 block goes back through
 // (1/4) D H16 (same butterfly order) before the cast.
@@ -499,6 +699,36 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t st) {
                              : launch_q2<kGridUniform, kRoundRTNE>(a, st);
   return a.rnd == kRoundSR ? launch_q2<kGridE2M1, kRoundSR>(a, st)
                            : launch_q2<kGridE2M1, kRoundRTNE>(a, st);
+}
+
+template <int GRID, int RND>
+static hipError_t launch_dual_t(const DualArgs &a, hipStream_t st) {
+  const int64_t n_ptiles = (a.kpad_c + kColTileRows - 1) / kColTileRows;
+  const int64_t n_ctiles = (a.n_cols + kColTileCols - 1) / kColTileCols;
+  const int64_t n_stack = a.col_axis == 2 ? a.n_groups : 1;
+  const int64_t rows_per = a.n_rows / n_stack;
+  const int blocks = grid_for(n_ptiles * n_ctiles * n_stack, 1, 256 * 8);
+  const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0) &&
+                   (a.n_cols % 2 == 0);
+  const bool grouped = a.goff != nullptr;
+#define UFP4_QD(V, G) \
+  hipLaunchKernelGGL((quant_dual_kernel<GRID, RND, V, G>), dim3(blocks), dim3(256), 0, st, a, \
+                     rows_per, n_stack)
+  if (vec) {
+    if (grouped) UFP4_QD(true, true); else UFP4_QD(true, false);
+  } else {
+    if (grouped) UFP4_QD(false, true); else UFP4_QD(false, false);
+  }
+#undef UFP4_QD
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual(const DualArgs &a, hipStream_t st) {
+  if (a.grid == kGridUniform)
+    return a.rnd == kRoundSR ? launch_dual_t<kGridUniform, kRoundSR>(a, st)
+                             : launch_dual_t<kGridUniform, kRoundRTNE>(a, st);
+  return a.rnd == kRoundSR ? launch_dual_t<kGridE2M1, kRoundSR>(a, st)
+                           : launch_dual_t<kGridE2M1, kRoundRTNE>(a, st);
 }
 
 hipError_t launch_dequantize(const uint8_t *codes, const float *scales, int64_t rows,

@@ -24,6 +24,30 @@ struct QuantArgs {
 constexpr int kMaxGroupsApi = 1024;
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
+// Dual-axis quantization: the row-wise operand (blocks along columns) and
+// the column-wise one (axis 1 or 2, with groups / stacking as QuantArgs) from
+// one read of x.  Signs are 0 for a side without RHT.
+struct DualArgs {
+  const uint16_t *x;
+  int64_t n_rows, n_cols, ld;
+  int col_axis;             // 1 along rows (transposed), 2 stacked
+  const int64_t *goff;      // device group offsets or nullptr (axis 1 only)
+  int n_groups;
+  int grid, rnd;
+  uint32_t seed_lo, seed_hi;
+  int rht_r;                // row-wise output
+  uint32_t mask_r, sid_r;
+  int64_t kpad_r;
+  uint8_t *codes_r;
+  float *scales_r;
+  int rht_c;                // column-wise output
+  uint32_t mask_c, sid_c;
+  int64_t kpad_c;
+  uint8_t *codes_c;
+  float *scales_c;
+};
+
+hipError_t launch_quantize_dual(const DualArgs &a, hipStream_t st);
 hipError_t launch_dequantize(const uint8_t *codes, const float *scales, int64_t rows,
                              int64_t kpad, int grid, bool inverse, uint32_t sign_mask, float *out,
                              int64_t ld_out, hipStream_t st);

@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Tuple
 
 import torch
 
@@ -27,7 +27,7 @@ STATUS = {0: "UFP4_OK", -1: "UFP4_ERR_INVALID_ARG", -2: "UFP4_ERR_SHAPE",
           -3: "UFP4_ERR_MISMATCH", -4: "UFP4_ERR_UNSUPPORTED", -5: "UFP4_ERR_HIP"}
 
 # Every symbol include/ufp4.h declares.
-EXPORTS = ("ufp4_rht_quantize", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
+EXPORTS = ("ufp4_rht_quantize", "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
            "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_workspace_size",
            "ufp4_status_string")
 
@@ -36,6 +36,12 @@ class UFP4Error(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {STATUS.get(status, status)}")
         self.status = status
+
+
+class QuantSide(ctypes.Structure):
+    """Mirror of ufp4_quant_side."""
+    _fields_ = [("rht", ctypes.c_int32), ("sign_mask", ctypes.c_uint32),
+                ("stream_id", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
 
 
 class QTensorDesc(ctypes.Structure):
@@ -63,6 +69,9 @@ def lib() -> ctypes.CDLL:
     Q = ctypes.POINTER(QTensorDesc)
     L.ufp4_rht_quantize.argtypes = [P, I64, I64, I64, I32, P, I32, I32, U32, I32, I32, U64, U32,
                                     Q, P]
+    L.ufp4_rht_quantize_dual.argtypes = [P, I64, I64, I64, I32, P, I32, I32, I32, U64,
+                                         ctypes.POINTER(QuantSide), ctypes.POINTER(QuantSide),
+                                         Q, Q, P]
     L.ufp4_dequantize.argtypes = [Q, I32, P, I64, P]
     L.ufp4_gemm_fprop.argtypes = [Q, Q, P, I64, P]
     L.ufp4_gemm_dgrad.argtypes = [Q, Q, P, I64, P]
@@ -72,7 +81,7 @@ def lib() -> ctypes.CDLL:
     L.ufp4_workspace_size.restype = ctypes.c_size_t
     L.ufp4_status_string.argtypes = [I32]
     L.ufp4_status_string.restype = ctypes.c_char_p
-    for f in ("ufp4_rht_quantize", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
+    for f in ("ufp4_rht_quantize", "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
               "ufp4_gemm_wgrad", "ufp4_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int32
     _lib = L
@@ -115,6 +124,36 @@ def padded_k_capacity(n_rows: int, n_groups: int) -> int:
     return (n_rows + 15 * n_groups + 15) // 16 * 16
 
 
+def _quant_shape(x: torch.Tensor, axis: int, group_offsets: Optional[torch.Tensor],
+                 kpad: Optional[int], n_groups: int):
+    """(rows, kpad, n_groups) of the quantized output of x along `axis`."""
+    assert x.dim() == 2 and x.dtype == torch.bfloat16 and x.is_cuda and x.stride(1) == 1
+    n_rows, n_cols = x.shape
+    if axis != BLOCKS_ALONG_ROWS_STACKED:
+        n_groups = 0
+    if axis == BLOCKS_ALONG_COLS:
+        return n_rows, (n_cols + 15) // 16 * 16, 0
+    if axis == BLOCKS_ALONG_ROWS_STACKED:
+        assert n_groups >= 1 and n_rows % n_groups == 0
+        return n_cols * n_groups, (n_rows // n_groups + 15) // 16 * 16, n_groups
+    if group_offsets is not None:
+        assert group_offsets.dtype == torch.int64 and group_offsets.is_cuda
+        n_groups = group_offsets.numel() - 1
+        kp = kpad if kpad is not None else padded_k_capacity(n_rows, n_groups)
+        return n_cols, kp, n_groups
+    return n_cols, (n_rows + 15) // 16 * 16, 0
+
+
+def _out_desc(out: Optional[Quantized], rows: int, kp: int, device):
+    if out is not None:
+        assert out.rows == rows and out.kpad == kp
+        codes, scales = out.codes, out.scales
+    else:
+        codes = torch.empty((rows, kp // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, kp // 16), dtype=torch.float32, device=device)
+    return codes, scales, QTensorDesc(codes.data_ptr(), scales.data_ptr(), rows, 0, kp, 0, 0, 0, 0)
+
+
 def ufp4_rht_quantize(x: torch.Tensor, axis: int = BLOCKS_ALONG_COLS, rht: bool = True,
                       sign_mask: int = 0, grid: int = GRID_UNIFORM, rnd: int = ROUND_RTNE,
                       seed: int = 0, stream_id: int = 0,
@@ -124,35 +163,41 @@ def ufp4_rht_quantize(x: torch.Tensor, axis: int = BLOCKS_ALONG_COLS, rht: bool 
     """Quantize a 2-D bf16 CUDA tensor (any row stride, unit column stride).
     `out` reuses the buffers of an earlier result of the same shape;
     `n_groups` is the number of equal row groups for BLOCKS_ALONG_ROWS_STACKED."""
-    assert x.dim() == 2 and x.dtype == torch.bfloat16 and x.is_cuda and x.stride(1) == 1
+    rows, kp, n_groups = _quant_shape(x, axis, group_offsets, kpad, n_groups)
+    codes, scales, d = _out_desc(out, rows, kp, x.device)
     n_rows, n_cols = x.shape
-    if axis != BLOCKS_ALONG_ROWS_STACKED:
-        n_groups = 0
-    if axis == BLOCKS_ALONG_COLS:
-        rows, kp = n_rows, (n_cols + 15) // 16 * 16
-    elif axis == BLOCKS_ALONG_ROWS_STACKED:
-        assert n_groups >= 1 and n_rows % n_groups == 0
-        rows, kp = n_cols * n_groups, (n_rows // n_groups + 15) // 16 * 16
-    else:
-        rows = n_cols
-        if group_offsets is not None:
-            assert group_offsets.dtype == torch.int64 and group_offsets.is_cuda
-            n_groups = group_offsets.numel() - 1
-            kp = kpad if kpad is not None else padded_k_capacity(n_rows, n_groups)
-        else:
-            kp = (n_rows + 15) // 16 * 16
-    if out is not None:
-        assert out.rows == rows and out.kpad == kp
-        codes, scales = out.codes, out.scales
-    else:
-        codes = torch.empty((rows, kp // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((rows, kp // 16), dtype=torch.float32, device=x.device)
-    d = QTensorDesc(codes.data_ptr(), scales.data_ptr(), rows, 0, kp, 0, 0, 0, 0)
     st = lib().ufp4_rht_quantize(_ptr(x), n_rows, n_cols, x.stride(0), axis,
                                  _ptr(group_offsets), n_groups, int(rht), sign_mask, grid, rnd,
                                  seed, stream_id, ctypes.byref(d), _stream(x.device))
     _check(st, "ufp4_rht_quantize")
     return Quantized(codes, scales, rows, d.k, kp, d.grid, d.rht, d.sign_mask)
+
+
+def ufp4_rht_quantize_dual(x: torch.Tensor, rowwise: Tuple[bool, int, int],
+                           colwise: Tuple[bool, int, int], col_axis: int = BLOCKS_ALONG_ROWS,
+                           grid: int = GRID_UNIFORM, rnd: int = ROUND_RTNE, seed: int = 0,
+                           group_offsets: Optional[torch.Tensor] = None,
+                           kpad: Optional[int] = None, n_groups: int = 0,
+                           out_rows: Optional[Quantized] = None,
+                           out_cols: Optional[Quantized] = None) -> Tuple[Quantized, Quantized]:
+    """Both operands of x from one read: (row-wise, column-wise).  `rowwise`
+    and `colwise` are (rht, sign_mask, stream_id) of each output; the
+    column-wise output follows `col_axis`, `group_offsets`, `kpad` and
+    `n_groups` exactly as ufp4_rht_quantize does."""
+    rr, kr, _ = _quant_shape(x, BLOCKS_ALONG_COLS, None, None, 0)
+    rc, kc, n_groups = _quant_shape(x, col_axis, group_offsets, kpad, n_groups)
+    codes_r, scales_r, dr = _out_desc(out_rows, rr, kr, x.device)
+    codes_c, scales_c, dc = _out_desc(out_cols, rc, kc, x.device)
+    sr = QuantSide(int(rowwise[0]), rowwise[1], rowwise[2], 0)
+    sc = QuantSide(int(colwise[0]), colwise[1], colwise[2], 0)
+    n_rows, n_cols = x.shape
+    st = lib().ufp4_rht_quantize_dual(_ptr(x), n_rows, n_cols, x.stride(0), col_axis,
+                                      _ptr(group_offsets), n_groups, grid, rnd, seed,
+                                      ctypes.byref(sr), ctypes.byref(sc), ctypes.byref(dr),
+                                      ctypes.byref(dc), _stream(x.device))
+    _check(st, "ufp4_rht_quantize_dual")
+    return (Quantized(codes_r, scales_r, rr, dr.k, kr, dr.grid, dr.rht, dr.sign_mask),
+            Quantized(codes_c, scales_c, rc, dc.k, kc, dc.grid, dc.rht, dc.sign_mask))
 
 
 def ufp4_dequantize(q: Quantized, inverse_rht: bool = False) -> torch.Tensor:
