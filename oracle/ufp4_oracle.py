@@ -24,6 +24,12 @@ Impact, and UFP4 Recipe"):
   bits, 1 mantissa bit; uniform E1M2/INT4 grid has equal spacing).
 * paperlayer.ai summary, section 4 and 7: UFP4 = uniform grid, RHT on all
   three GEMMs, stochastic rounding on dY only.
+* Diagnostics (``quant_stats``, ``output_stats``, ``stats_summary``):
+  paperlayer.ai section 3.2, section 5 Q1 and appendix A (tensor and
+  GEMM-output SQNR, their change under RHT, effective bucket utilization);
+  gist.science technical summary (attenuation factor alpha < 1 of a GEMM);
+  the dreamwings.cn post, section on the RHT turning point (quantization
+  underflow ratio, bucket utilization of E2M1's 15 codes).
 
 Where the pages leave a step open the reading taken here is stated next to
 the step.  All "FP32" steps are separate numpy float32 operations (numpy
@@ -501,4 +507,101 @@ def conditional_level_bias(m: np.ndarray, idx: np.ndarray, grid: int) -> dict:
         if sel.any():
             out[float(L[i])] = (float(np.mean(L[i] - m[sel])), int(sel.sum()),
                                 float(np.std(L[i] - m[sel])))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics (paperlayer summary section 3.2, section 5 Q1 and appendix A:
+# tensor and GEMM-output SQNR and its change under RHT, bucket utilization;
+# gist.science technical summary: the attenuation factor alpha of a GEMM;
+# dreamwings.cn post, "RHT turning point": the quantization underflow ratio
+# and the use of E2M1's 15 buckets).  Readings (the pages give no formulas):
+#   * every sum runs over the tensor's logical elements (padding excluded),
+#     pairing each input x with its dequantized value xhat in the input's own
+#     domain: the dequantized block goes back through (1/4) D H16 in float64
+#     when the quantization used the RHT;
+#   * SQNR = 10 log10(sum x^2 / sum (xhat - x)^2), alpha = <xhat, x>/<x, x>,
+#     delta_mag = (sum |xhat| - sum |x|) / sum |x|;
+#   * underflow: an element whose pre-rounding value y (after the RHT, as the
+#     quantizer computes it in FP32) is nonzero but whose magnitude index is
+#     0; the ratio is over the elements with y != 0;
+#   * bucket utilization: exp(H)/15 with H the entropy (natural log) of the
+#     empirical distribution of the 15 signed codes -- 1 when all codes are
+#     equally used, 1/15 when one is; the raw 16-bin nibble histogram is kept.
+# ---------------------------------------------------------------------------
+STAT_KEYS = ("sum_x2", "sum_err2", "sum_x_xhat", "sum_abs_x", "sum_abs_xhat")
+
+
+def quant_stats(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, axis: int,
+                rht: bool, sign_mask: int, grid: int) -> dict:
+    """Sums and counts comparing bf16 input x [n_rows, n_cols] with its
+    quantization (codes, scales) along `axis` (AXIS_COLS or AXIS_ROWS, one
+    group)."""
+    assert axis in (AXIS_COLS, AXIS_ROWS)
+    x = bf16_bits_to_f32(x_bits)
+    kvalid = x.shape[1] if axis == AXIS_COLS else x.shape[0]
+    xb = to_blocked_rows(x, axis)                       # [rows, K_p] FP32, zero padded
+    rows, kp = xb.shape
+    blocks = xb.reshape(rows, kp // BLOCK, BLOCK)
+    y = (rht16(blocks, sign_mask) if rht else blocks).reshape(rows, kp)
+    v = dequantize64(codes, scales, grid)
+    if rht:
+        H = sylvester_hadamard(4)
+        d = signs_from_mask(sign_mask).astype(np.float64)
+        v = (0.25 * (v.reshape(rows, kp // BLOCK, BLOCK) @ H.T) * d).reshape(rows, kp)
+    keep = np.arange(kp) < kvalid
+    x64 = xb.astype(np.float64)[:, keep]
+    xh = v[:, keep]
+    nib = unpack_nibbles(codes)[:, keep]
+    yk = y[:, keep]
+    nz = yk != 0
+    return {
+        "sum_x2": float((x64 * x64).sum()),
+        "sum_err2": float(((xh - x64) ** 2).sum()),
+        "sum_x_xhat": float((x64 * xh).sum()),
+        "sum_abs_x": float(np.abs(x64).sum()),
+        "sum_abs_xhat": float(np.abs(xh).sum()),
+        "n_elems": int(x64.size),
+        "n_nonzero": int(nz.sum()),
+        "n_underflow": int((nz & ((nib & 7) == 0)).sum()),
+        "hist": np.bincount(nib.ravel(), minlength=16).astype(np.int64),
+    }
+
+
+def output_stats(ref: np.ndarray, test: np.ndarray) -> dict:
+    """The same sums for a GEMM output `test` against its reference `ref`
+    (x -> ref, xhat -> test); counts other than n_elems are zero."""
+    r = np.asarray(ref, dtype=np.float64)
+    t = np.asarray(test, dtype=np.float64)
+    return {
+        "sum_x2": float((r * r).sum()),
+        "sum_err2": float(((t - r) ** 2).sum()),
+        "sum_x_xhat": float((r * t).sum()),
+        "sum_abs_x": float(np.abs(r).sum()),
+        "sum_abs_xhat": float(np.abs(t).sum()),
+        "n_elems": int(r.size),
+        "n_nonzero": 0,
+        "n_underflow": 0,
+        "hist": np.zeros(16, dtype=np.int64),
+    }
+
+
+def stats_summary(st: dict) -> dict:
+    """Derived metrics of a quant_stats / output_stats result."""
+    out = {
+        "sqnr_db": (float(10.0 * np.log10(st["sum_x2"] / st["sum_err2"]))
+                    if st["sum_err2"] > 0 else float("inf")),
+        "one_minus_alpha": float(1.0 - st["sum_x_xhat"] / st["sum_x2"]),
+        "delta_mag": float((st["sum_abs_xhat"] - st["sum_abs_x"]) / st["sum_abs_x"]),
+        "underflow_ratio": (st["n_underflow"] / st["n_nonzero"]) if st["n_nonzero"] else 0.0,
+    }
+    h = np.asarray(st["hist"], dtype=np.float64).copy()
+    h[0] += h[8]          # +0 and -0 are one bucket (the quantizer never emits -0)
+    h[8] = 0.0
+    tot = h.sum()
+    if tot > 0:
+        p = h[h > 0] / tot
+        out["bucket_utilization"] = float(np.exp(-(p * np.log(p)).sum()) / 15.0)
+    else:
+        out["bucket_utilization"] = 0.0
     return out
