@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -82,12 +83,13 @@ def parse():
                     help="single: six single-axis quantizations per step; dual: three dual-axis "
                          "quantizations (one read of X, W and dY each, both operands out)")
     ap.add_argument("--workload", default="dense-1.5b",
-                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b", "copy"],
+                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b", "copy", "q1-outputs"],
                     help="dense-1.5b: the timed step (default); quant-sweep: the 2^28-element "
                          "quantizer sweep, one JSON line per case; moe-*: the expert layers "
                          "(grouped GEMMs), one JSON line; copy: a plain 1 GiB device copy, the "
                          "streaming ceiling and the calibration run of the HBM traffic "
-                         "counters")
+                         "counters; q1-outputs: GEMM-output SQNR of each recipe against the "
+                         "unquantized product, one JSON line per GEMM")
     return ap.parse_args()
 
 
@@ -311,26 +313,45 @@ class MoeStep(Step):
         return 2.0 * self.tokens * self.H * self.F
 
 
+def diag_summary(st: dict) -> dict:
+    """Reported metrics from the diagnostics kernel's sums and counts (the
+    formulas of ufp4_stats in include/ufp4.h)."""
+    out = {"sqnr_db": (10.0 * math.log10(st["sum_x2"] / st["sum_err2"])
+                       if st["sum_err2"] > 0 else None),
+           "one_minus_alpha": 1.0 - st["sum_x_xhat"] / st["sum_x2"],
+           "delta_mag": (st["sum_abs_xhat"] - st["sum_abs_x"]) / st["sum_abs_x"]}
+    if st["n_nonzero"]:
+        out["underflow_ratio"] = st["n_underflow"] / st["n_nonzero"]
+        h = list(st["hist"])
+        h[0] += h[8]
+        h[8] = 0
+        tot = float(sum(h))
+        ent = -sum((c / tot) * math.log(c / tot) for c in h if c)
+        out["bucket_utilization"] = math.exp(ent) / 15.0
+    return out
+
+
 def quant_sweep(args):
     """The quantizer sweep: 16384 x 16384 bf16 (Gaussian, Laplace, Student-t3)
-    x {RHT, none} x {uniform, E2M1} x {RTNE, SR} x {row-wise, column-wise}.
+    x {row-wise, column-wise} x {uniform, E2M1} x {RTNE, SR} x {none, RHT}.
     Each case is timed with HIP events over `steps` calls after `warmup`; the
     tensor (512 MiB) does not fit the 256 MiB MALL, so every call streams from
-    HBM.  Also reports 1 - alpha and SQNR of the dequantized (inverse-RHT)
-    tensor against the input, computed with torch reductions as diagnostics."""
+    HBM.  Each case also reports the pages' quantization diagnostics from the
+    library's diagnostics kernel (SQNR, 1 - alpha, delta_mag, underflow ratio,
+    bucket utilization) and, for the RHT case, the SQNR change RHT brings."""
     import torch
     from uniform_grid_fp4_amd import ufp4 as U
     from uniform_grid_fp4_amd import workloads as W
     dev = torch.device("cuda:0")
     n = W.SWEEP_SHAPE[0] * W.SWEEP_SHAPE[1]
+    ws = torch.empty(U.ufp4_stats_workspace_size() // 8, dtype=torch.int64, device=dev)
     for dist in W.SWEEP_DISTS:
         x = W.sweep_tensor(dist, dev)
-        xf = x.double()
-        ex = float((xf * xf).sum())
         for axis in (U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS):
-            for rht in (True, False):
-                for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
-                    for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+            for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
+                for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+                    sqnr_plain = None
+                    for rht in (False, True):
                         q = U.ufp4_rht_quantize(x, axis, rht, 0xBEEF, grid, rnd, 7, 0)
                         for _ in range(args.warmup):
                             U.ufp4_rht_quantize(x, axis, rht, 0xBEEF, grid, rnd, 7, 0, out=q)
@@ -342,12 +363,11 @@ def quant_sweep(args):
                         e1.record()
                         torch.cuda.synchronize()
                         ms = e0.elapsed_time(e1) / args.steps
-                        xh = U.ufp4_dequantize(q, inverse_rht=rht).double()
-                        if axis == U.BLOCKS_ALONG_ROWS:
-                            xh = xh.t()
-                        dot = float((xh * xf).sum())
-                        err = float(((xh - xf) ** 2).sum())
-                        del xh
+                        diag = diag_summary(U.ufp4_quant_stats(x, q, axis, workspace=ws))
+                        if rht and sqnr_plain is not None and diag["sqnr_db"] is not None:
+                            diag["delta_sqnr_db"] = diag["sqnr_db"] - sqnr_plain
+                        else:
+                            sqnr_plain = diag["sqnr_db"]
                         gbs = n * BYTES_PER_QUANT_ELEM / (ms * 1e-3) / 1e9
                         print(json.dumps({
                             "workload": "quant-sweep", "dist": dist,
@@ -356,10 +376,55 @@ def quant_sweep(args):
                             "rht": rht, "grid": "uniform" if grid == 0 else "e2m1",
                             "rounding": "sr" if rnd else "rtne", "us": round(ms * 1e3, 2),
                             "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                            "one_minus_alpha": dot and 1.0 - dot / ex,
-                            "sqnr_db": 10.0 * __import__("math").log10(ex / err)}), flush=True)
-        del x, xf
+                            **diag}), flush=True)
+                        del q
+        del x
         torch.cuda.empty_cache()
+
+
+def q1_outputs(args):
+    """The pages' single-GEMM output test on the dense 1.5B layer: the three
+    GEMM outputs of each recipe (uniform or E2M1 grid, with or without the
+    RHT; stochastic rounding on dY) against the unquantized product of the
+    bf16 operands (FP32 torch matmul, the reference only), as SQNR, 1 - alpha
+    and the SQNR change RHT brings -- measured with the library's
+    diagnostics kernel.  One JSON line per (GEMM, grid, RHT)."""
+    import torch
+    from uniform_grid_fp4_amd import ufp4 as U
+    from uniform_grid_fp4_amd import workloads as W
+    dev = torch.device("cuda:0")
+    L = W.dense_1p5b(dev)
+    mf, md, mw = L.masks
+    x, w, dy = L.x.float(), L.w.float(), L.dy.float()
+    refs = {"fprop": torch.matmul(x, w.t().contiguous()),
+            "dgrad": torch.matmul(dy, w),
+            "wgrad": torch.matmul(dy.t().contiguous(), x)}
+    del x, w, dy
+    ws = torch.empty(U.ufp4_stats_workspace_size() // 8, dtype=torch.int64, device=dev)
+    C, R = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS
+    for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
+        plain = {}
+        for rht in (False, True):
+            qx = U.ufp4_rht_quantize(L.x, C, rht, mf, grid)
+            qw = U.ufp4_rht_quantize(L.w, C, rht, mf, grid)
+            qdy = U.ufp4_rht_quantize(L.dy, C, rht, md, grid, U.ROUND_SR, 1234, 0)
+            qwt = U.ufp4_rht_quantize(L.w, R, rht, md, grid)
+            qdyt = U.ufp4_rht_quantize(L.dy, R, rht, mw, grid, U.ROUND_SR, 1234, 1)
+            qxt = U.ufp4_rht_quantize(L.x, R, rht, mw, grid)
+            outs = {"fprop": U.ufp4_gemm_fprop(qx, qw), "dgrad": U.ufp4_gemm_dgrad(qdy, qwt),
+                    "wgrad": U.ufp4_gemm_wgrad(qdyt, qxt)}
+            for name, y in outs.items():
+                d = diag_summary(U.ufp4_output_stats(refs[name], y, workspace=ws))
+                line = {"workload": "q1-outputs", "layer": L.name, "gemm": name,
+                        "grid": "uniform" if grid == 0 else "e2m1", "rht": rht,
+                        "sqnr_db": d["sqnr_db"], "one_minus_alpha": d["one_minus_alpha"]}
+                if rht:
+                    line["delta_sqnr_db"] = d["sqnr_db"] - plain[name]
+                else:
+                    plain[name] = d["sqnr_db"]
+                print(json.dumps(line), flush=True)
+            del outs, qx, qw, qdy, qwt, qdyt, qxt
+            torch.cuda.empty_cache()
 
 
 def copy_ceiling(args):
@@ -398,6 +463,8 @@ def main():
         return quant_sweep(args)
     if args.workload == "copy":
         return copy_ceiling(args)
+    if args.workload == "q1-outputs":
+        return q1_outputs(args)
     import torch
     from uniform_grid_fp4_amd import ufp4 as U
     from uniform_grid_fp4_amd import workloads as W

@@ -228,6 +228,58 @@ ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_g
                               int64_t ldc, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* Diagnostics of the pages' quantization-quality measurements
+ * (paperlayer.ai section 3.2, section 5 Q1 and appendix A: tensor and
+ * GEMM-output SQNR and its change under RHT, bucket utilization;
+ * gist.science technical summary: a GEMM's attenuation factor alpha;
+ * dreamwings.cn post: the quantization underflow ratio).  Raw sums and
+ * counts, written to DEVICE memory; from them, on the host:
+ *   SQNR [dB]          = 10 log10(sum_x2 / sum_err2)
+ *   alpha              = sum_x_xhat / sum_x2          (1 - alpha: shrinkage)
+ *   delta_mag          = (sum_abs_xhat - sum_abs_x) / sum_abs_x
+ *   underflow ratio    = n_underflow / n_nonzero
+ *   bucket utilization = exp(H) / 15, H the entropy of hist with bins 0 and 8
+ *                        merged (the 15 signed codes).
+ * Sums are FP64 and bitwise reproducible (fixed reduction order). */
+typedef struct {
+  double sum_x2;       /* sum x^2 (reference values)                          */
+  double sum_err2;     /* sum (xhat - x)^2                                    */
+  double sum_x_xhat;   /* sum x * xhat                                        */
+  double sum_abs_x;    /* sum |x|                                             */
+  double sum_abs_xhat; /* sum |xhat|                                          */
+  uint64_t n_elems;    /* logical elements compared (padding excluded)        */
+  uint64_t n_nonzero;  /* elements whose rotated pre-rounding value is != 0   */
+  uint64_t n_underflow;/* ... of which the magnitude index is 0               */
+  uint64_t hist[16];   /* nibble histogram of the logical elements            */
+} ufp4_stats;
+
+/* Workspace bytes every diagnostics call needs (a constant). */
+size_t ufp4_stats_workspace_size(void);
+
+/* ufp4_quant_stats -- compare the bf16 input x [n_rows, n_cols] (stride ld)
+ * with its quantization q, made by ufp4_rht_quantize along `axis`
+ * (ALONG_COLS, or ALONG_ROWS with one group).  Each logical element x is
+ * paired with xhat = its dequantized value taken back to x's domain (the
+ * block's inverse RHT (1/4) D H16 in FP64 when q->rht).  An element
+ * underflows when y, its value after the RHT exactly as the quantizer
+ * computes it in FP32 (y = x without RHT), is nonzero and its magnitude index
+ * is 0.  workspace: device, >= ufp4_stats_workspace_size() bytes, 8-byte
+ * aligned, overwritten.  d_out: device ufp4_stats, 8-byte aligned.
+ * Returns OK, INVALID_ARG (null, misaligned, bad axis, workspace too small),
+ * SHAPE (q does not match x and axis), HIP. */
+ufp4_status ufp4_quant_stats(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
+                             int32_t axis, const ufp4_qtensor *q, void *workspace,
+                             size_t workspace_bytes, ufp4_stats *d_out, hipStream_t stream);
+
+/* ufp4_output_stats -- the same sums for a GEMM output `test` [rows, cols]
+ * (stride ld_test) against a reference output `ref` (stride ld_ref), FP32
+ * device arrays: x = ref, xhat = test; n_nonzero, n_underflow and hist are 0.
+ * Workspace and d_out as for ufp4_quant_stats.  Returns OK, INVALID_ARG,
+ * SHAPE, HIP. */
+ufp4_status ufp4_output_stats(const float *ref, int64_t ld_ref, const float *test,
+                              int64_t ld_test, int64_t rows, int64_t cols, void *workspace,
+                              size_t workspace_bytes, ufp4_stats *d_out, hipStream_t stream);
+
 /* Bytes of workspace a GEMM call can use to split K (0 if it never does). */
 size_t ufp4_workspace_size(int32_t kind, int64_t m, int64_t n, int64_t kpad, int32_t n_groups);
 

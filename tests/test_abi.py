@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     decl = declared_functions()
-    assert len(decl) == 9, decl
+    assert len(decl) == 12, decl
     assert sorted(U.EXPORTS) == decl
     L = U.lib()
     for name in decl:
@@ -155,3 +155,42 @@ def dual(**kw):
 ])
 def test_dual_quantize_rejects(kw, expect):
     assert dual(**kw) == expect
+
+
+def test_stats_workspace_size_is_a_constant():
+    assert U.ufp4_stats_workspace_size() == 1024 * 24 * 8
+
+
+def qstats(**kw):
+    a = dict(x=FAKE, n_rows=32, n_cols=48, ld=48, axis=0, q=fake_desc(rows=32, k=48, kpad=48),
+             ws=ctypes.c_void_p(0x20000), nbytes=U.ufp4_stats_workspace_size(),
+             out=ctypes.c_void_p(0x30000))
+    a.update(kw)
+    return U.lib().ufp4_quant_stats(a["x"], a["n_rows"], a["n_cols"], a["ld"], a["axis"],
+                                    ctypes.byref(a["q"]), a["ws"], a["nbytes"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), -1), (dict(ws=None), -1), (dict(out=None), -1),
+    (dict(ws=ctypes.c_void_p(0x20004)), -1), (dict(out=ctypes.c_void_p(0x30004)), -1),
+    (dict(nbytes=1024), -1),                       # workspace too small
+    (dict(axis=2), -1), (dict(axis=7), -1),
+    (dict(q=fake_desc(rows=32, k=48, kpad=64)), -2),   # kpad must be roundup16(k)
+    (dict(q=fake_desc(rows=31, k=48, kpad=48)), -2),
+    (dict(axis=1), -2),                            # transposed: rows = n_cols, k = n_rows
+    (dict(ld=40), -2), (dict(n_rows=0), -2),
+])
+def test_quant_stats_rejects(kw, expect):
+    assert qstats(**kw) == expect
+
+
+def test_output_stats_rejects():
+    L = U.lib()
+    ws, n, out = ctypes.c_void_p(0x20000), U.ufp4_stats_workspace_size(), ctypes.c_void_p(0x30000)
+    f = L.ufp4_output_stats
+    assert f(None, 8, FAKE, 8, 4, 8, ws, n, out, None) == -1
+    assert f(FAKE, 8, None, 8, 4, 8, ws, n, out, None) == -1
+    assert f(FAKE, 8, FAKE, 8, 4, 8, ws, n - 8, out, None) == -1
+    assert f(FAKE, 8, FAKE, 8, 4, 8, ws, n, ctypes.c_void_p(0x30002), None) == -1
+    assert f(FAKE, 4, FAKE, 8, 4, 8, ws, n, out, None) == -2
+    assert f(FAKE, 8, FAKE, 8, 0, 8, ws, n, out, None) == -2

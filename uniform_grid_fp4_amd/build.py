@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libufp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "stats.hip"]
 
 # -ffp-contract=off: no multiply-add fusion anywhere (the quantizer's two
 #   roundings r = RN(g/s), t = RN(y*r) must stay separate).

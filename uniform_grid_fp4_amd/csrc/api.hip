@@ -11,6 +11,7 @@ using namespace ufp4;
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 int64_t round_up16(int64_t n) { return (n + 15) / 16 * 16; }
 
 ufp4_status check_qtensor(const ufp4_qtensor *q) {
@@ -262,6 +263,57 @@ ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_g
   }
   if (ldc < g.N) return UFP4_ERR_SHAPE;
   return launch_gemm(g, stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
+}
+
+static_assert(sizeof(ufp4_stats) == sizeof(StatsPartial), "ufp4_stats layout");
+
+size_t ufp4_stats_workspace_size(void) { return (size_t)kStatsMaxBlocks * sizeof(StatsPartial); }
+
+ufp4_status ufp4_quant_stats(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
+                             int32_t axis, const ufp4_qtensor *q, void *workspace,
+                             size_t workspace_bytes, ufp4_stats *d_out, hipStream_t stream) {
+  ufp4_status s = check_qtensor(q);
+  if (s != UFP4_OK) return s;
+  if (x_bf16 == nullptr || workspace == nullptr || d_out == nullptr) return UFP4_ERR_INVALID_ARG;
+  if (!aligned8(workspace) || !aligned8(d_out)) return UFP4_ERR_INVALID_ARG;
+  if (workspace_bytes < ufp4_stats_workspace_size()) return UFP4_ERR_INVALID_ARG;
+  if (axis != UFP4_BLOCKS_ALONG_COLS && axis != UFP4_BLOCKS_ALONG_ROWS)
+    return UFP4_ERR_INVALID_ARG;
+  if (n_rows <= 0 || n_cols <= 0 || ld < n_cols) return UFP4_ERR_SHAPE;
+  const int64_t rows = axis == UFP4_BLOCKS_ALONG_COLS ? n_rows : n_cols;
+  const int64_t k = axis == UFP4_BLOCKS_ALONG_COLS ? n_cols : n_rows;
+  if (q->rows != rows || q->k != k || q->kpad != round_up16(k)) return UFP4_ERR_SHAPE;
+  StatsArgs a{};
+  a.x = x_bf16;
+  a.ld = ld;
+  a.axis = axis;
+  a.rows = rows;
+  a.kpad = q->kpad;
+  a.kvalid = k;
+  a.codes = q->codes;
+  a.scales = q->scales;
+  a.grid = q->grid;
+  a.rht = q->rht;
+  a.sign_mask = q->rht ? q->sign_mask : 0u;
+  return launch_quant_stats(a, static_cast<StatsPartial *>(workspace),
+                            reinterpret_cast<StatsPartial *>(d_out), stream) == hipSuccess
+             ? UFP4_OK
+             : UFP4_ERR_HIP;
+}
+
+ufp4_status ufp4_output_stats(const float *ref, int64_t ld_ref, const float *test,
+                              int64_t ld_test, int64_t rows, int64_t cols, void *workspace,
+                              size_t workspace_bytes, ufp4_stats *d_out, hipStream_t stream) {
+  if (ref == nullptr || test == nullptr || workspace == nullptr || d_out == nullptr)
+    return UFP4_ERR_INVALID_ARG;
+  if (!aligned8(workspace) || !aligned8(d_out)) return UFP4_ERR_INVALID_ARG;
+  if (workspace_bytes < ufp4_stats_workspace_size()) return UFP4_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || ld_ref < cols || ld_test < cols) return UFP4_ERR_SHAPE;
+  return launch_output_stats(ref, ld_ref, test, ld_test, rows, cols,
+                             static_cast<StatsPartial *>(workspace),
+                             reinterpret_cast<StatsPartial *>(d_out), stream) == hipSuccess
+             ? UFP4_OK
+             : UFP4_ERR_HIP;
 }
 
 size_t ufp4_workspace_size(int32_t kind, int64_t m, int64_t n, int64_t kpad, int32_t n_groups) {

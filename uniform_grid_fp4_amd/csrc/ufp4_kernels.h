@@ -52,6 +52,33 @@ hipError_t launch_dequantize(const uint8_t *codes, const float *scales, int64_t 
                              int64_t kpad, int grid, bool inverse, uint32_t sign_mask, float *out,
                              int64_t ld_out, hipStream_t st);
 
+// Diagnostics: sums and counts comparing an input with its quantization
+// (axis 0 row-wise, 1 transposed, one group), or a GEMM output with its
+// reference.  Same layout as the public ufp4_stats.
+struct StatsPartial {
+  double sum[5];            // x^2, (xhat - x)^2, x * xhat, |x|, |xhat|
+  uint64_t n_elems, n_nonzero, n_underflow;
+  uint64_t hist[16];
+};
+constexpr int kStatsMaxBlocks = 1024;   // partials in the workspace
+
+struct StatsArgs {
+  const uint16_t *x;
+  int64_t ld;
+  int axis;
+  int64_t rows, kpad, kvalid;   // quantized rows, padded K, logical K
+  const uint8_t *codes;
+  const float *scales;
+  int grid, rht;
+  uint32_t sign_mask;
+};
+
+hipError_t launch_quant_stats(const StatsArgs &a, StatsPartial *workspace, StatsPartial *out,
+                              hipStream_t st);
+hipError_t launch_output_stats(const float *ref, int64_t ld_ref, const float *test,
+                               int64_t ld_test, int64_t rows, int64_t cols,
+                               StatsPartial *workspace, StatsPartial *out, hipStream_t st);
+
 // GEMM C = A * B^T on quantized K-contiguous operands.
 //   mode 0: dense, A [M, kpad], B [N, kpad], C [M, N].
 //   mode 1: grouped along M: A rows split by goff, B [n_groups*N, kpad].

@@ -27,9 +27,10 @@ STATUS = {0: "UFP4_OK", -1: "UFP4_ERR_INVALID_ARG", -2: "UFP4_ERR_SHAPE",
           -3: "UFP4_ERR_MISMATCH", -4: "UFP4_ERR_UNSUPPORTED", -5: "UFP4_ERR_HIP"}
 
 # Every symbol include/ufp4.h declares.
-EXPORTS = ("ufp4_rht_quantize", "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
-           "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_workspace_size",
-           "ufp4_status_string")
+EXPORTS = ("ufp4_rht_quantize", "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop",
+           "ufp4_gemm_dgrad", "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_workspace_size",
+           "ufp4_status_string", "ufp4_stats_workspace_size", "ufp4_quant_stats",
+           "ufp4_output_stats")
 
 
 class UFP4Error(RuntimeError):
@@ -79,9 +80,14 @@ def lib() -> ctypes.CDLL:
     L.ufp4_grouped_gemm.argtypes = [I32, I32, P, Q, Q, P, I64, P, ctypes.c_size_t, P]
     L.ufp4_workspace_size.argtypes = [I32, I64, I64, I64, I32]
     L.ufp4_workspace_size.restype = ctypes.c_size_t
+    L.ufp4_stats_workspace_size.argtypes = []
+    L.ufp4_stats_workspace_size.restype = ctypes.c_size_t
+    L.ufp4_quant_stats.argtypes = [P, I64, I64, I64, I32, Q, P, ctypes.c_size_t, P, P]
+    L.ufp4_output_stats.argtypes = [P, I64, P, I64, I64, I64, P, ctypes.c_size_t, P, P]
     L.ufp4_status_string.argtypes = [I32]
     L.ufp4_status_string.restype = ctypes.c_char_p
-    for f in ("ufp4_rht_quantize", "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
+    for f in ("ufp4_quant_stats", "ufp4_output_stats", "ufp4_rht_quantize",
+              "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
               "ufp4_gemm_wgrad", "ufp4_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int32
     _lib = L
@@ -198,6 +204,57 @@ def ufp4_rht_quantize_dual(x: torch.Tensor, rowwise: Tuple[bool, int, int],
     _check(st, "ufp4_rht_quantize_dual")
     return (Quantized(codes_r, scales_r, rr, dr.k, kr, dr.grid, dr.rht, dr.sign_mask),
             Quantized(codes_c, scales_c, rc, dc.k, kc, dc.grid, dc.rht, dc.sign_mask))
+
+
+STATS_SUMS = ("sum_x2", "sum_err2", "sum_x_xhat", "sum_abs_x", "sum_abs_xhat")
+STATS_COUNTS = ("n_elems", "n_nonzero", "n_underflow")
+
+
+def ufp4_stats_workspace_size() -> int:
+    return int(lib().ufp4_stats_workspace_size())
+
+
+def _stats_buffers(device, workspace: Optional[torch.Tensor]):
+    nbytes = ufp4_stats_workspace_size()
+    if workspace is None:
+        workspace = torch.empty(nbytes // 8, dtype=torch.int64, device=device)
+    out = torch.empty(24, dtype=torch.int64, device=device)   # one ufp4_stats
+    return workspace, workspace.numel() * workspace.element_size(), out
+
+
+def _stats_dict(out: torch.Tensor) -> dict:
+    h = out.cpu()
+    sums = h[:5].view(torch.float64).tolist()
+    d = dict(zip(STATS_SUMS, sums))
+    d.update(zip(STATS_COUNTS, (int(v) for v in h[5:8])))
+    d["hist"] = [int(v) for v in h[8:24]]
+    return d
+
+
+def ufp4_quant_stats(x: torch.Tensor, q: Quantized, axis: int = BLOCKS_ALONG_COLS,
+                     workspace: Optional[torch.Tensor] = None) -> dict:
+    """Sums and counts comparing x with its quantization q (see ufp4_stats in
+    include/ufp4.h); waits for the result."""
+    assert x.dim() == 2 and x.dtype == torch.bfloat16 and x.is_cuda and x.stride(1) == 1
+    ws, nbytes, out = _stats_buffers(x.device, workspace)
+    d = q.desc()
+    st = lib().ufp4_quant_stats(_ptr(x), x.shape[0], x.shape[1], x.stride(0), axis,
+                                ctypes.byref(d), _ptr(ws), nbytes, _ptr(out), _stream(x.device))
+    _check(st, "ufp4_quant_stats")
+    return _stats_dict(out)
+
+
+def ufp4_output_stats(ref: torch.Tensor, test: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None) -> dict:
+    """The same sums for a GEMM output `test` against `ref` (FP32, 2-D)."""
+    assert ref.shape == test.shape and ref.dim() == 2
+    assert ref.dtype == test.dtype == torch.float32 and ref.stride(1) == test.stride(1) == 1
+    ws, nbytes, out = _stats_buffers(ref.device, workspace)
+    st = lib().ufp4_output_stats(_ptr(ref), ref.stride(0), _ptr(test), test.stride(0),
+                                 ref.shape[0], ref.shape[1], _ptr(ws), nbytes, _ptr(out),
+                                 _stream(ref.device))
+    _check(st, "ufp4_output_stats")
+    return _stats_dict(out)
 
 
 def ufp4_dequantize(q: Quantized, inverse_rht: bool = False) -> torch.Tensor:
