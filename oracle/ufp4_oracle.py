@@ -50,16 +50,22 @@ import numpy as np
 # ---------------------------------------------------------------------------
 GRID_UNIFORM = 0
 GRID_E2M1 = 1
+GRID_E2M1_MAX2 = 2
 
 # Magnitude levels indexed by the 3-bit magnitude field of the nibble.
 #  uniform: the E1M2 magnitude field read as an integer, {0..7}; normalized
 #           codebook {-7..7}/7, gmax = 1 (levels scaled by g = 7 below).
 #  E2M1:    OCP E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; g = 6.
+#  E2M1 range-restricted to max_fpx = 2.0 (paperlayer summary section 5 Q4:
+#           the variant keeps only {0, 0.5, 1.0, 1.5, 2.0}): the block absmax
+#           maps to 2.0, g = 2; the nibbles are E2M1 bit patterns with a
+#           magnitude index of at most 4.
 LEVELS = {
     GRID_UNIFORM: np.arange(8, dtype=np.float64),
     GRID_E2M1: np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]),
+    GRID_E2M1_MAX2: np.array([0.0, 0.5, 1.0, 1.5, 2.0]),
 }
-GMAX = {GRID_UNIFORM: 7.0, GRID_E2M1: 6.0}
+GMAX = {GRID_UNIFORM: 7.0, GRID_E2M1: 6.0, GRID_E2M1_MAX2: 2.0}
 
 ROUND_RTNE = 0
 ROUND_SR = 1
@@ -247,9 +253,10 @@ def rtne_index(m: np.ndarray, grid: int) -> np.ndarray:
     deterministic tie-breaking; reading: ties to the even level index, which
     is IEEE round-half-even for both grids)."""
     L = LEVELS[grid]
+    top = len(L) - 1
     m = np.asarray(m, dtype=np.float64)   # float32 values, exact in float64
-    lo = np.clip(np.searchsorted(L, m, side="right") - 1, 0, 7)
-    hi = np.minimum(lo + 1, 7)
+    lo = np.clip(np.searchsorted(L, m, side="right") - 1, 0, top)
+    hi = np.minimum(lo + 1, top)
     dlo = m - L[lo]                      # exact: float32 minus a short level
     dhi = L[hi] - m
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0) & (hi != lo))
@@ -265,9 +272,10 @@ def sr_index(m: np.ndarray, grid: int, u32: np.ndarray) -> np.ndarray:
     level above and f = 0.
     """
     L = LEVELS[grid]
+    top = len(L) - 1
     m = np.asarray(m, dtype=np.float64)
-    lo = np.clip(np.searchsorted(L, m, side="right") - 1, 0, 7)
-    hi = np.minimum(lo + 1, 7)
+    lo = np.clip(np.searchsorted(L, m, side="right") - 1, 0, top)
+    hi = np.minimum(lo + 1, top)
     span = L[hi] - L[lo]
     f = np.where(hi == lo, 0.0, (m - L[lo]) / np.where(span == 0, 1.0, span))
     F = np.floor(f * 4294967296.0).astype(np.uint64)
@@ -381,8 +389,8 @@ def quantize(x_bits: np.ndarray, axis: int, rht: bool, sign_mask: int,
 def dequantize64(codes: np.ndarray, scales: np.ndarray, grid: int) -> np.ndarray:
     """Dequantized values in float64: sign * L[idx] * s / g, shape [rows, K_p]."""
     nib = unpack_nibbles(codes).astype(np.int64)
-    L = LEVELS[grid]
-    mag = L[nib & 7]
+    L = np.concatenate([LEVELS[grid], np.full(8 - len(LEVELS[grid]), np.nan)])
+    mag = L[nib & 7]          # an index past the grid's top level is no code: NaN
     sgn = np.where(nib & 8, -1.0, 1.0)
     rows, kp = nib.shape
     s = np.repeat(np.asarray(scales, dtype=np.float64), BLOCK, axis=-1).reshape(rows, kp)

@@ -20,7 +20,7 @@ def rand_bits(rng, shape, scale=1.0):
     return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("grid", [O.GRID_UNIFORM, O.GRID_E2M1])
+@pytest.mark.parametrize("grid", [O.GRID_UNIFORM, O.GRID_E2M1, O.GRID_E2M1_MAX2])
 def test_gemm_equals_brute_force_sum_over_codes(grid):
     rng = np.random.default_rng(200)
     a = rand_bits(rng, (3, 40))

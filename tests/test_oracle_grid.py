@@ -77,7 +77,34 @@ def test_e2m1_grid_round_trip(e):
     assert (scales == np.float32(6 * 2.0 ** e)).all()
 
 
-@pytest.mark.parametrize("grid", [O.GRID_UNIFORM, O.GRID_E2M1])
+ALL_GRIDS = [O.GRID_UNIFORM, O.GRID_E2M1, O.GRID_E2M1_MAX2]
+
+
+def test_range_restricted_e2m1_levels_match_pages():
+    # section 5 Q4: the max_fpx = 2.0 variant keeps only {0, 0.5, 1.0, 1.5, 2.0}
+    L = O.LEVELS[O.GRID_E2M1_MAX2]
+    assert list(L) == [0.0, 0.5, 1.0, 1.5, 2.0] and O.GMAX[O.GRID_E2M1_MAX2] == 2.0
+    full = O.LEVELS[O.GRID_E2M1]
+    assert list(L) == list(full[full <= 2.0])      # the same E2M1 bit patterns
+
+
+@pytest.mark.parametrize("e", [-130, -80, 0, 100])
+def test_range_restricted_e2m1_round_trip(e):
+    L = O.LEVELS[O.GRID_E2M1_MAX2]
+    rng = np.random.default_rng(25 + abs(e))
+    i = rng.integers(0, 5, size=(64, 16))
+    sgn = np.where(rng.random((64, 16)) < 0.5, -1, 1)
+    i[:, 5] = 4
+    x = (sgn * L[i] * 2.0 ** e).astype(np.float32)
+    codes, scales, _ = O.quantize(to_bits(x), O.AXIS_COLS, False, 0, O.GRID_E2M1_MAX2,
+                                  O.ROUND_RTNE)
+    nib = O.unpack_nibbles(codes).astype(np.int64)
+    expect = np.where(i == 0, 0, ((sgn < 0).astype(np.int64) << 3) | i)
+    assert (nib == expect).all() and (nib & 7).max() == 4
+    assert (scales == np.float32(2 * 2.0 ** e)).all()
+
+
+@pytest.mark.parametrize("grid", ALL_GRIDS)
 def test_rtne_matches_brute_force(grid):
     L = O.LEVELS[grid]
     g = np.float32(O.GMAX[grid])
@@ -97,9 +124,11 @@ def test_rtne_ties_go_to_even_index():
     # E2M1 ties: 0.25->0, 0.75->1.0, 1.25->1.0, 1.75->2.0, 2.5->2, 3.5->4, 5->4
     e = O.rtne_index(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32), O.GRID_E2M1)
     assert list(O.LEVELS[O.GRID_E2M1][e]) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    r = O.rtne_index(np.array([0.25, 0.75, 1.25, 1.75, 2.0], np.float32), O.GRID_E2M1_MAX2)
+    assert list(O.LEVELS[O.GRID_E2M1_MAX2][r]) == [0.0, 1.0, 1.0, 2.0, 2.0]
 
 
-@pytest.mark.parametrize("grid", [O.GRID_UNIFORM, O.GRID_E2M1])
+@pytest.mark.parametrize("grid", ALL_GRIDS)
 def test_every_bf16_value_in_a_block_with_unit_normalization(grid):
     """Block [x, g, 0, ...]: the scale is g so r = 1 and t = x exactly; the code
     of x must be the brute-force nearest level of |x| with x's sign.  Runs over
@@ -145,7 +174,7 @@ def test_zero_block_and_negative_zero():
 
 
 @pytest.mark.parametrize("rht", [False, True])
-@pytest.mark.parametrize("grid", [O.GRID_UNIFORM, O.GRID_E2M1])
+@pytest.mark.parametrize("grid", ALL_GRIDS)
 def test_codes_invariant_under_power_of_two_scaling(rht, grid):
     """Absmax scaling makes codes invariant under exact power-of-two scaling
     of a block; the tiny-scale branch (s < 2^-64) must keep that property."""
@@ -178,7 +207,7 @@ def test_dequantize_values():
     rng = np.random.default_rng(50)
     x = rng.standard_normal((8, 32)).astype(np.float32)
     b = (x.view(np.uint32) >> 16).astype(np.uint16)
-    for grid in (O.GRID_UNIFORM, O.GRID_E2M1):
+    for grid in ALL_GRIDS:
         codes, scales, _ = O.quantize(b, O.AXIS_COLS, True, 0x00FF, grid, O.ROUND_RTNE)
         v = O.dequantize(codes, scales, grid)
         nib = O.unpack_nibbles(codes)

@@ -86,7 +86,8 @@ def test_sr_word_selection_matches_pytorch_engine_stream(torch_philox):
 
 
 @pytest.mark.parametrize("grid,ts", [(O.GRID_UNIFORM, [0.3, 2.5, 6.9]),
-                                     (O.GRID_E2M1, [0.3, 1.2, 2.4, 5.0])])
+                                     (O.GRID_E2M1, [0.3, 1.2, 2.4, 5.0]),
+                                     (O.GRID_E2M1_MAX2, [0.3, 1.2, 1.9])])
 def test_sr_is_unbiased(grid, ts):
     N = 10_000_000
     L = O.LEVELS[grid]
@@ -106,7 +107,7 @@ def test_sr_is_unbiased(grid, ts):
 
 
 def test_sr_on_a_level_never_moves():
-    for grid in (O.GRID_UNIFORM, O.GRID_E2M1):
+    for grid in (O.GRID_UNIFORM, O.GRID_E2M1, O.GRID_E2M1_MAX2):
         L = O.LEVELS[grid].astype(np.float32)
         m = np.repeat(L, 1000)
         u = O.sr_random_u32(np.arange(m.size, dtype=np.uint64), 5, 0)
