@@ -382,13 +382,26 @@ def quant_sweep(args):
         torch.cuda.empty_cache()
 
 
+# Recipes of the single-GEMM output comparison: grid, and which GEMMs'
+# operands get the RHT (paperlayer summary section 4 and section 5 Q4: UFP4
+# applies it to all three; the E2M1 reference recipe to WGRAD only; the
+# range-restricted E2M1 variant keeps {0, .5, 1, 1.5, 2} with full RHT).
+Q1_RECIPES = (
+    ("uniform, no RHT", 0, (False, False, False)),
+    ("UFP4: uniform, RHT on all GEMMs", 0, (True, True, True)),
+    ("E2M1, no RHT", 1, (False, False, False)),
+    ("E2M1, RHT on WGRAD only (reference recipe)", 1, (False, False, True)),
+    ("E2M1, RHT on all GEMMs", 1, (True, True, True)),
+    ("E2M1 max 2.0, RHT on all GEMMs", 2, (True, True, True)),
+)
+
+
 def q1_outputs(args):
     """The pages' single-GEMM output test on the dense 1.5B layer: the three
-    GEMM outputs of each recipe (uniform or E2M1 grid, with or without the
-    RHT; stochastic rounding on dY) against the unquantized product of the
-    bf16 operands (FP32 torch matmul, the reference only), as SQNR, 1 - alpha
-    and the SQNR change RHT brings -- measured with the library's
-    diagnostics kernel.  One JSON line per (GEMM, grid, RHT)."""
+    GEMM outputs of each recipe (grid and RHT placement; stochastic rounding
+    on dY) against the unquantized product of the bf16 operands (FP32 torch
+    matmul, the reference only), as SQNR and 1 - alpha -- measured with the
+    library's diagnostics kernel.  One JSON line per (recipe, GEMM)."""
     import torch
     from uniform_grid_fp4_amd import ufp4 as U
     from uniform_grid_fp4_amd import workloads as W
@@ -402,29 +415,22 @@ def q1_outputs(args):
     del x, w, dy
     ws = torch.empty(U.ufp4_stats_workspace_size() // 8, dtype=torch.int64, device=dev)
     C, R = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS
-    for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
-        plain = {}
-        for rht in (False, True):
-            qx = U.ufp4_rht_quantize(L.x, C, rht, mf, grid)
-            qw = U.ufp4_rht_quantize(L.w, C, rht, mf, grid)
-            qdy = U.ufp4_rht_quantize(L.dy, C, rht, md, grid, U.ROUND_SR, 1234, 0)
-            qwt = U.ufp4_rht_quantize(L.w, R, rht, md, grid)
-            qdyt = U.ufp4_rht_quantize(L.dy, R, rht, mw, grid, U.ROUND_SR, 1234, 1)
-            qxt = U.ufp4_rht_quantize(L.x, R, rht, mw, grid)
-            outs = {"fprop": U.ufp4_gemm_fprop(qx, qw), "dgrad": U.ufp4_gemm_dgrad(qdy, qwt),
-                    "wgrad": U.ufp4_gemm_wgrad(qdyt, qxt)}
-            for name, y in outs.items():
-                d = diag_summary(U.ufp4_output_stats(refs[name], y, workspace=ws))
-                line = {"workload": "q1-outputs", "layer": L.name, "gemm": name,
-                        "grid": "uniform" if grid == 0 else "e2m1", "rht": rht,
-                        "sqnr_db": d["sqnr_db"], "one_minus_alpha": d["one_minus_alpha"]}
-                if rht:
-                    line["delta_sqnr_db"] = d["sqnr_db"] - plain[name]
-                else:
-                    plain[name] = d["sqnr_db"]
-                print(json.dumps(line), flush=True)
-            del outs, qx, qw, qdy, qwt, qdyt, qxt
-            torch.cuda.empty_cache()
+    for name, grid, (hf, hd, hw) in Q1_RECIPES:
+        qx = U.ufp4_rht_quantize(L.x, C, hf, mf, grid)
+        qw = U.ufp4_rht_quantize(L.w, C, hf, mf, grid)
+        qdy = U.ufp4_rht_quantize(L.dy, C, hd, md, grid, U.ROUND_SR, 1234, 0)
+        qwt = U.ufp4_rht_quantize(L.w, R, hd, md, grid)
+        qdyt = U.ufp4_rht_quantize(L.dy, R, hw, mw, grid, U.ROUND_SR, 1234, 1)
+        qxt = U.ufp4_rht_quantize(L.x, R, hw, mw, grid)
+        outs = {"fprop": U.ufp4_gemm_fprop(qx, qw), "dgrad": U.ufp4_gemm_dgrad(qdy, qwt),
+                "wgrad": U.ufp4_gemm_wgrad(qdyt, qxt)}
+        for gemm, y in outs.items():
+            d = diag_summary(U.ufp4_output_stats(refs[gemm], y, workspace=ws))
+            print(json.dumps({"workload": "q1-outputs", "layer": L.name, "recipe": name,
+                              "gemm": gemm, "sqnr_db": d["sqnr_db"],
+                              "one_minus_alpha": d["one_minus_alpha"]}), flush=True)
+        del outs, qx, qw, qdy, qwt, qdyt, qxt
+        torch.cuda.empty_cache()
 
 
 def copy_ceiling(args):

@@ -61,8 +61,12 @@ typedef enum {
  *  UNIFORM: E1M2/INT4 grid {-7..7}/7 times the scale; the nibble's 3-bit
  *           magnitude field is the integer level k (the E1M2 bit layout).
  *  E2M1:    the OCP E2M1 grid {0,.5,1,1.5,2,3,4,6}/6 times the scale; the
- *           nibble is the E2M1 bit pattern. */
-typedef enum { UFP4_GRID_UNIFORM = 0, UFP4_GRID_E2M1 = 1 } ufp4_grid;
+ *           nibble is the E2M1 bit pattern.
+ *  E2M1_MAX2: range-restricted E2M1 with max_fpx = 2.0 (paperlayer.ai
+ *           section 5 "Q4: Recipe ablations"): only {0,.5,1,1.5,2}, i.e.
+ *           {0,.5,1,1.5,2}/2 times the scale; E2M1 bit patterns with a
+ *           magnitude index of at most 4. */
+typedef enum { UFP4_GRID_UNIFORM = 0, UFP4_GRID_E2M1 = 1, UFP4_GRID_E2M1_MAX2 = 2 } ufp4_grid;
 
 /* Rounding (paperlayer.ai summary, section 2 "Rounding rules").
  *  RTNE: nearest level, ties to the even level index.
@@ -133,8 +137,8 @@ typedef struct {
  *   h = 1,2,4,8 in FP32, then the exact 1/4) with D from the mask.
  * grid, rnd, seed, stream_id: see the enums above (seed/stream_id ignored
  *   for RTNE).
- * Per block: s = max|y| (stored), r = RN(g/s) with g = 7 (uniform) or 6
- *   (E2M1), t = RN(y*r) -- two roundings, no FMA; blocks with
+ * Per block: s = max|y| (stored), r = RN(g/s) with g = 7 (uniform), 6
+ *   (E2M1) or 2 (E2M1_MAX2), t = RN(y*r) -- two roundings, no FMA; blocks with
  *   0 < s < 2^-64 use y*2^64 and s*2^64 in that step (the stored scale is s).
  * Returns UFP4_OK, INVALID_ARG (null pointer, bad enum, codes/scales not
  *   16-byte aligned, reserved != 0), SHAPE (non-positive size, ld < n_cols,
@@ -197,7 +201,7 @@ ufp4_status ufp4_dequantize(const ufp4_qtensor *q, int32_t inverse_rht, float *o
  *   C[m, n] = sum_kb sa[m,kb] * sb[n,kb] * (sum_{k in kb} qa*qb) / g^2
  * over the operands' common kpad.  Operands must agree on k, kpad, grid, rht
  * and sign_mask (else UFP4_ERR_MISMATCH), which is what makes the rotation
- * cancel.  Both grids are accepted.
+ * cancel.  All three grids are accepted.
  *   FPROP: A = X  [T, H] (blocks along H), B = W   [F, H]  -> Y  [T, F]
  *   DGRAD: A = dY [T, F] (blocks along F), B = W^T [H, F] (W quantized with
  *          ALONG_ROWS) -> dX [T, H]

@@ -88,6 +88,8 @@ def test_gemm_validation(name):
     ok = fake_desc()
     assert gemm(fn, ok, fake_desc(k=16, kpad=16)) == -3        # K mismatch
     assert gemm(fn, ok, fake_desc(grid=1)) == -3               # grid mismatch
+    assert gemm(fn, ok, fake_desc(grid=2)) == -3
+    assert gemm(fn, fake_desc(grid=3), fake_desc(grid=3)) == -1   # no such grid
     assert gemm(fn, ok, fake_desc(rht=0)) == -3
     assert gemm(fn, ok, fake_desc(mask=0x4321)) == -3          # rotation would not cancel
     assert gemm(fn, ok, fake_desc(kpad=40)) == -2              # kpad % 16
@@ -143,7 +145,7 @@ def dual(**kw):
     (dict(rs=U.QuantSide(1, 0, 0, 7)), -1),           # reserved
     (dict(cs=U.QuantSide(2, 0, 0, 0)), -1),           # rht not 0/1
     (dict(rs=U.QuantSide(1, 0x10000, 0, 0)), -1),     # mask > 16 bits
-    (dict(grid=2), -1), (dict(rnd=5), -1),
+    (dict(grid=3), -1), (dict(rnd=5), -1),
     (dict(outc=fake_desc(rows=48, kpad=32)), -1),     # shares the row-wise buffers
     (dict(outr=fake_desc(rows=32, kpad=32)), -2),     # row-wise kpad must be 48
     (dict(outc=fake_desc(rows=32, kpad=32, codes=0x3000, scales=0x4000)), -2),  # rows = n_cols

@@ -70,7 +70,7 @@ SIDES = [((True, 0x1357, 0), (True, 0xBEEF, 1)), ((False, 0x1357, 0), (True, 0xB
          ((True, 0x00F0, 3), (False, 0, 0)), ((False, 0, 0), (False, 0, 2))]
 
 
-@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1, U.GRID_E2M1_MAX2])
 @pytest.mark.parametrize("rnd", [U.ROUND_RTNE, U.ROUND_SR])
 @pytest.mark.parametrize("sides", SIDES)
 def test_tiny_layer_tensors(grid, rnd, sides):
@@ -121,7 +121,7 @@ def test_stacked_columnwise(e, rows, cols):
                col_axis=U.BLOCKS_ALONG_ROWS_STACKED, n_groups=e, what="stacked")
 
 
-@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1, U.GRID_E2M1_MAX2])
 @pytest.mark.parametrize("rnd", [U.ROUND_RTNE, U.ROUND_SR])
 def test_special_values(grid, rnd):
     xd = dev_bf16(special_values_tensor())

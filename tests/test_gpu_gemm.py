@@ -47,7 +47,7 @@ def ref_gemm(a, b, grid=U.GRID_UNIFORM):
     return O.gemm_tn(host(a.codes), host(a.scales), host(b.codes), host(b.scales), grid)
 
 
-@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1, U.GRID_E2M1_MAX2])
 def test_tiny_layer_all_three_gemms(grid):
     L = W.tiny(DEV)
     mf, md, mw = L.masks

@@ -17,8 +17,8 @@ from uniform_grid_fp4_amd import workloads as W
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-COMBOS = [(g, r, h) for g in (U.GRID_UNIFORM, U.GRID_E2M1) for r in (U.ROUND_RTNE, U.ROUND_SR)
-          for h in (False, True)]
+GRIDS = (U.GRID_UNIFORM, U.GRID_E2M1, U.GRID_E2M1_MAX2)
+COMBOS = [(g, r, h) for g in GRIDS for r in (U.ROUND_RTNE, U.ROUND_SR) for h in (False, True)]
 
 
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
@@ -66,7 +66,8 @@ def test_colwise_tiny_workload(grid, rnd, rht):
 def test_ragged_shapes(shape, axis):
     g = torch.Generator(device=DEV).manual_seed(11)
     x = torch.randn(shape, device=DEV, generator=g).to(torch.bfloat16)
-    for grid, rnd, rht in [(0, 0, True), (0, 1, True), (1, 0, False), (1, 1, True)]:
+    for grid, rnd, rht in [(0, 0, True), (0, 1, True), (1, 0, False), (1, 1, True), (2, 0, True),
+                           (2, 1, False)]:
         check_quant(x, axis, rht, 0xB7E1, grid, rnd, 5, 2, what="ragged")
 
 
@@ -104,7 +105,7 @@ def test_special_values(grid, rnd, rht):
     check_quant(xd, U.BLOCKS_ALONG_ROWS, rht, 0x8001, grid, rnd, 21, 0, what="special^T")
 
 
-@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+@pytest.mark.parametrize("grid", GRIDS)
 def test_every_bf16_value_in_a_unit_block(grid):
     g = O.GMAX[grid]
     allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
@@ -142,7 +143,7 @@ def test_grouped_colwise(counts, rnd):
     assert q.kpad == U.padded_k_capacity(T, len(counts))
 
 
-@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+@pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("axis", [U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS])
 def test_dequantize(grid, axis):
     g = torch.Generator(device=DEV).manual_seed(15)

@@ -36,7 +36,7 @@ def check(x, axis, rht, mask, grid, rnd, what=""):
     return got
 
 
-@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1, U.GRID_E2M1_MAX2])
 @pytest.mark.parametrize("rnd", [U.ROUND_RTNE, U.ROUND_SR])
 @pytest.mark.parametrize("rht", [False, True])
 @pytest.mark.parametrize("axis", [U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS])
@@ -56,7 +56,7 @@ def test_ragged_and_strided(shape):
         check(x, axis, False, 0, U.GRID_E2M1, U.ROUND_RTNE, "ragged")
 
 
-@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1])
+@pytest.mark.parametrize("grid", [U.GRID_UNIFORM, U.GRID_E2M1, U.GRID_E2M1_MAX2])
 def test_special_values(grid):
     x = dev_bf16(special_values_tensor())
     for axis in (U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS):

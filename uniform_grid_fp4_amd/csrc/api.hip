@@ -18,7 +18,8 @@ ufp4_status check_qtensor(const ufp4_qtensor *q) {
   if (q == nullptr || q->codes == nullptr || q->scales == nullptr) return UFP4_ERR_INVALID_ARG;
   if (!aligned16(q->codes) || !aligned16(q->scales) || q->reserved != 0)
     return UFP4_ERR_INVALID_ARG;
-  if (q->grid != UFP4_GRID_UNIFORM && q->grid != UFP4_GRID_E2M1) return UFP4_ERR_INVALID_ARG;
+  if (q->grid != UFP4_GRID_UNIFORM && q->grid != UFP4_GRID_E2M1 && q->grid != UFP4_GRID_E2M1_MAX2)
+    return UFP4_ERR_INVALID_ARG;
   if (q->rht != 0 && q->rht != 1) return UFP4_ERR_INVALID_ARG;
   if (q->rows <= 0 || q->kpad <= 0 || q->kpad % 16 != 0 || q->k <= 0 || q->k > q->kpad)
     return UFP4_ERR_SHAPE;
@@ -72,7 +73,8 @@ ufp4_status check_quant(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, 
   if (axis != UFP4_BLOCKS_ALONG_COLS && axis != UFP4_BLOCKS_ALONG_ROWS &&
       axis != UFP4_BLOCKS_ALONG_ROWS_STACKED)
     return UFP4_ERR_INVALID_ARG;
-  if (grid != UFP4_GRID_UNIFORM && grid != UFP4_GRID_E2M1) return UFP4_ERR_INVALID_ARG;
+  if (grid != UFP4_GRID_UNIFORM && grid != UFP4_GRID_E2M1 && grid != UFP4_GRID_E2M1_MAX2)
+    return UFP4_ERR_INVALID_ARG;
   if (rnd != UFP4_ROUND_RTNE && rnd != UFP4_ROUND_SR) return UFP4_ERR_INVALID_ARG;
   if (rht != 0 && rht != 1) return UFP4_ERR_INVALID_ARG;
   if (sign_mask > 0xFFFFu) return UFP4_ERR_INVALID_ARG;

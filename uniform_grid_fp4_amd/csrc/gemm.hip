@@ -223,7 +223,9 @@ struct Gemm {
         __syncthreads();
       }
     }
-    constexpr float inv_g2 = (GRID == kGridUniform) ? (1.0f / 49.0f) : (1.0f / 144.0f);
+    // 1/g^2, with the E2M1 levels doubled in FP8: 1/(2*6)^2 and 1/(2*2)^2
+    constexpr float inv_g2 = (GRID == kGridUniform) ? (1.0f / 49.0f)
+                             : (GRID == kGridE2M1) ? (1.0f / 144.0f) : (1.0f / 16.0f);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave % kWavesM, wn = wave / kWavesM;
@@ -448,9 +450,14 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
     if (g.mode == 1) UFP4_G(kGridUniform, 1);
     UFP4_G(kGridUniform, 2);
   }
-  if (g.mode == 0) UFP4_G(kGridE2M1, 0);
-  if (g.mode == 1) UFP4_G(kGridE2M1, 1);
-  UFP4_G(kGridE2M1, 2);
+  if (g.grid == kGridE2M1) {
+    if (g.mode == 0) UFP4_G(kGridE2M1, 0);
+    if (g.mode == 1) UFP4_G(kGridE2M1, 1);
+    UFP4_G(kGridE2M1, 2);
+  }
+  if (g.mode == 0) UFP4_G(kGridE2M1Max2, 0);
+  if (g.mode == 1) UFP4_G(kGridE2M1Max2, 1);
+  UFP4_G(kGridE2M1Max2, 2);
 #undef UFP4_G
 }
 

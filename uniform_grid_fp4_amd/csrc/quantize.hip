@@ -585,7 +585,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     const int64_t kb = b - row * kblocks;
     const uint2 c = *reinterpret_cast<const uint2 *>(codes + b * 8);
     const double s = (double)scales[b];
-    constexpr double g = (GRID == kGridUniform) ? 7.0 : 6.0;
+    constexpr double g = (double)grid_g<GRID>();
     double d[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -697,8 +697,11 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t st) {
   if (a.grid == kGridUniform)
     return a.rnd == kRoundSR ? launch_q2<kGridUniform, kRoundSR>(a, st)
                              : launch_q2<kGridUniform, kRoundRTNE>(a, st);
-  return a.rnd == kRoundSR ? launch_q2<kGridE2M1, kRoundSR>(a, st)
-                           : launch_q2<kGridE2M1, kRoundRTNE>(a, st);
+  if (a.grid == kGridE2M1)
+    return a.rnd == kRoundSR ? launch_q2<kGridE2M1, kRoundSR>(a, st)
+                             : launch_q2<kGridE2M1, kRoundRTNE>(a, st);
+  return a.rnd == kRoundSR ? launch_q2<kGridE2M1Max2, kRoundSR>(a, st)
+                           : launch_q2<kGridE2M1Max2, kRoundRTNE>(a, st);
 }
 
 template <int GRID, int RND>
@@ -727,8 +730,11 @@ hipError_t launch_quantize_dual(const DualArgs &a, hipStream_t st) {
   if (a.grid == kGridUniform)
     return a.rnd == kRoundSR ? launch_dual_t<kGridUniform, kRoundSR>(a, st)
                              : launch_dual_t<kGridUniform, kRoundRTNE>(a, st);
-  return a.rnd == kRoundSR ? launch_dual_t<kGridE2M1, kRoundSR>(a, st)
-                           : launch_dual_t<kGridE2M1, kRoundRTNE>(a, st);
+  if (a.grid == kGridE2M1)
+    return a.rnd == kRoundSR ? launch_dual_t<kGridE2M1, kRoundSR>(a, st)
+                             : launch_dual_t<kGridE2M1, kRoundRTNE>(a, st);
+  return a.rnd == kRoundSR ? launch_dual_t<kGridE2M1Max2, kRoundSR>(a, st)
+                           : launch_dual_t<kGridE2M1Max2, kRoundRTNE>(a, st);
 }
 
 hipError_t launch_dequantize(const uint8_t *codes, const float *scales, int64_t rows,
@@ -741,8 +747,10 @@ hipError_t launch_dequantize(const uint8_t *codes, const float *scales, int64_t 
                      rows, kblocks, out, ld_out, sign_mask)
   if (grid == kGridUniform) {
     if (inverse) UFP4_DQ(kGridUniform, true); else UFP4_DQ(kGridUniform, false);
-  } else {
+  } else if (grid == kGridE2M1) {
     if (inverse) UFP4_DQ(kGridE2M1, true); else UFP4_DQ(kGridE2M1, false);
+  } else {
+    if (inverse) UFP4_DQ(kGridE2M1Max2, true); else UFP4_DQ(kGridE2M1Max2, false);
   }
 #undef UFP4_DQ
   return hipGetLastError();

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kStatsThreads) void quant_stats_kernel(const StatsA
   for (int i = 0; i < 3; ++i) acc.n[i] = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc.h[i] = 0;
-  constexpr double g = (GRID == kGridUniform) ? 7.0 : 6.0;
+  constexpr double g = (double)grid_g<GRID>();
   const int64_t kblocks = a.kpad / 16;
   const int64_t nblk = a.rows * kblocks;
   const int64_t stride = (int64_t)gridDim.x * kStatsThreads;
@@ -242,9 +242,12 @@ hipError_t launch_quant_stats(const StatsArgs &a, StatsPartial *workspace, Stats
   if (a.grid == kGridUniform)
     hipLaunchKernelGGL((quant_stats_kernel<kGridUniform>), dim3(blocks), dim3(kStatsThreads), 0,
                        st, a, workspace);
-  else
+  else if (a.grid == kGridE2M1)
     hipLaunchKernelGGL((quant_stats_kernel<kGridE2M1>), dim3(blocks), dim3(kStatsThreads), 0, st,
                        a, workspace);
+  else
+    hipLaunchKernelGGL((quant_stats_kernel<kGridE2M1Max2>), dim3(blocks), dim3(kStatsThreads), 0,
+                       st, a, workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kStatsThreads), 0, st, workspace, blocks,

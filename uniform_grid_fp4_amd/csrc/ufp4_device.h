@@ -15,7 +15,15 @@
 
 namespace ufp4 {
 
-enum { kGridUniform = 0, kGridE2M1 = 1 };
+enum { kGridUniform = 0, kGridE2M1 = 1, kGridE2M1Max2 = 2 };
+
+// Largest normalized magnitude g of a grid: the block absmax maps to g.
+// Range-restricted E2M1 keeps the E2M1 levels up to 2.0 (and their bit
+// patterns), so it shares E2M1's rounding below 2.
+template <int GRID>
+__host__ __device__ constexpr float grid_g() {
+  return GRID == kGridUniform ? 7.0f : (GRID == kGridE2M1 ? 6.0f : 2.0f);
+}
 enum { kRoundRTNE = 0, kRoundSR = 1 };
 
 // ---------------------------------------------------------------------------
@@ -175,7 +183,7 @@ __device__ __forceinline__ void quantize_block(float (&v)[16], uint64_t idx0, ui
   for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
   const float s = RHT ? amax * 0.25f : amax;   // exact
   scale = s;
-  constexpr float g = (GRID == kGridUniform) ? 7.0f : 6.0f;
+  constexpr float g = grid_g<GRID>();
   float post;
   if (s >= 0x1p-64f) {
     const float r = g / s;                     // correctly rounded division
@@ -230,7 +238,10 @@ __device__ __forceinline__ void quantize_block(float (&v)[16], uint64_t idx0, ui
           const uint32_t F = (uint32_t)((mc - fl) * 4294967296.0f);
           k[j] = __float_as_uint(fl + 12582912.0f) + (r < F ? 1u : 0u);
         } else {
-          k[j] = (RND == kRoundSR) ? e2m1_sr(m, r) : e2m1_rtne(m);
+          // m <= g up to one ulp; RTNE rounds that ulp back to g, SR must not
+          // round past the top level
+          k[j] = (RND == kRoundSR) ? e2m1_sr(GRID == kGridE2M1Max2 ? fminf(m, 2.0f) : m, r)
+                                   : e2m1_rtne(m);
         }
       }
       const uint32_t mags = interleave_nibbles(gather_b0(k[0], k[2], k[4], k[6]),

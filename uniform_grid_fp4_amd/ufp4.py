@@ -18,7 +18,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libufp4.so")
 
-GRID_UNIFORM, GRID_E2M1 = 0, 1
+GRID_UNIFORM, GRID_E2M1, GRID_E2M1_MAX2 = 0, 1, 2
 ROUND_RTNE, ROUND_SR = 0, 1
 BLOCKS_ALONG_COLS, BLOCKS_ALONG_ROWS, BLOCKS_ALONG_ROWS_STACKED = 0, 1, 2
 FPROP, DGRAD, WGRAD = 0, 1, 2
