@@ -217,6 +217,19 @@ ufp4_status ufp4_gemm_wgrad(const ufp4_qtensor *dytq, const ufp4_qtensor *xtq, f
                             int64_t lddw, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* Output element type of the GEMM calls with an out_dtype argument.
+ *  F32:  the FP32 result, as the calls above write it.
+ *  BF16: that FP32 result rounded to bf16, nearest even (bf16 bit patterns;
+ *        the epilogue of a bf16 training step, half the output traffic). */
+typedef enum { UFP4_OUT_F32 = 0, UFP4_OUT_BF16 = 1 } ufp4_out_dtype;
+
+/* ufp4_gemm_out -- FPROP (kind 0), DGRAD (1) or WGRAD (2) as above, with the
+ * output element type chosen by out_dtype (ldc in elements).  c must be
+ * aligned to its element size.  Returns OK, INVALID_ARG, SHAPE, MISMATCH,
+ * HIP. */
+ufp4_status ufp4_gemm_out(int32_t kind, const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
+                          int32_t out_dtype, int64_t ldc, hipStream_t stream);
+
 /* ufp4_grouped_gemm -- the expert-grouped (MoE) form.
  * kind 0 (FPROP) / 1 (DGRAD): rows of A are split into n_groups groups by the
  *   device int64 offsets d_group_offsets[n_groups+1] (first 0, last a->rows);
@@ -286,6 +299,12 @@ ufp4_status ufp4_output_stats(const float *ref, int64_t ld_ref, const float *tes
 
 /* Bytes of workspace a GEMM call can use to split K (0 if it never does). */
 size_t ufp4_workspace_size(int32_t kind, int64_t m, int64_t n, int64_t kpad, int32_t n_groups);
+
+/* ufp4_grouped_gemm_out -- ufp4_grouped_gemm with the output element type
+ * chosen by out_dtype (ufp4_out_dtype; ldc in elements) and no workspace. */
+ufp4_status ufp4_grouped_gemm_out(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
+                                  const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
+                                  int32_t out_dtype, int64_t ldc, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char *ufp4_status_string(ufp4_status status);

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     decl = declared_functions()
-    assert len(decl) == 12, decl
+    assert len(decl) == 14, decl
     assert sorted(U.EXPORTS) == decl
     L = U.lib()
     for name in decl:
@@ -196,3 +196,22 @@ def test_output_stats_rejects():
     assert f(FAKE, 8, FAKE, 8, 4, 8, ws, n, ctypes.c_void_p(0x30002), None) == -1
     assert f(FAKE, 4, FAKE, 8, 4, 8, ws, n, out, None) == -2
     assert f(FAKE, 8, FAKE, 8, 0, 8, ws, n, out, None) == -2
+
+
+def test_gemm_out_validation():
+    L = U.lib()
+    ok = fake_desc()
+    f = L.ufp4_gemm_out
+    assert f(3, ctypes.byref(ok), ctypes.byref(ok), FAKE, 0, 32, None) == -1     # kind
+    assert f(0, ctypes.byref(ok), ctypes.byref(ok), FAKE, 2, 32, None) == -1     # dtype
+    assert f(0, ctypes.byref(ok), ctypes.byref(ok), None, 1, 32, None) == -1
+    assert f(0, ctypes.byref(ok), ctypes.byref(ok), ctypes.c_void_p(0x10001), 1, 32, None) == -1
+    assert f(0, ctypes.byref(ok), ctypes.byref(ok), ctypes.c_void_p(0x10002), 0, 32, None) == -1
+    assert f(1, ctypes.byref(ok), ctypes.byref(fake_desc(grid=1)), FAKE, 1, 32, None) == -3
+    assert f(2, ctypes.byref(ok), ctypes.byref(ok), FAKE, 1, 16, None) == -2     # ldc < N
+    g = L.ufp4_grouped_gemm_out
+    assert g(0, 2, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 5, 32, None) == -1
+    assert g(0, 2, None, ctypes.byref(ok), ctypes.byref(ok), FAKE, 1, 32, None) == -1
+    assert g(0, 0, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 1, 32, None) == -2
+    assert g(1, 2, FAKE, ctypes.byref(ok), ctypes.byref(ok), ctypes.c_void_p(0x10001), 1, 32,
+             None) == -1

@@ -135,3 +135,37 @@ def test_grouped_wgrad(counts):
     for e, c in enumerate(counts):
         if c == 0:
             assert (host(dw[e]) == 0).all()
+
+
+@pytest.mark.parametrize("kind", [U.FPROP, U.DGRAD, U.WGRAD])
+@pytest.mark.parametrize("m,n,k", [(130, 70, 48), (300, 200, 1040), (1, 1, 16)])
+def test_bf16_epilogue_rounds_the_fp32_result(kind, m, n, k):
+    print(f"[gemm] bf16 epilogue kind={kind} {m}x{n}x{k}", flush=True)
+    a, b = rand_bf16((m, k), 5), rand_bf16((n, k), 6, 0.02)
+    aq, bq = qrow(a, 0x2DB4), qrow(b, 0x2DB4)
+    f32 = U.ufp4_gemm_out(kind, aq, bq, torch.float32)
+    assert torch.equal(f32, U.ufp4_gemm_fprop(aq, bq))
+    bf = U.ufp4_gemm_out(kind, aq, bq, torch.bfloat16)
+    assert bf.dtype == torch.bfloat16 and torch.equal(bf, f32.to(torch.bfloat16))
+    big = torch.zeros((m, n + 9), dtype=torch.bfloat16, device=DEV)
+    U.ufp4_gemm_out(kind, aq, bq, out=big[:, 4:4 + n])
+    assert torch.equal(big[:, 4:4 + n], bf)
+    assert (big[:, :4] == 0).all() and (big[:, 4 + n:] == 0).all()
+
+
+def test_grouped_bf16_epilogue():
+    counts = [40, 0, 70, 18]
+    off = torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int64, device=DEV)
+    T, E, H, F = sum(counts), len(counts), 96, 80
+    x, w = rand_bf16((T, H), 7), rand_bf16((E * F, H), 8, 0.02)
+    xq, wq = qrow(x, 0x0F1E), qrow(w, 0x0F1E)
+    for kind, a, b in ((U.FPROP, xq, wq),):
+        f32 = U.ufp4_grouped_gemm(kind, off, a, b)
+        bf = U.ufp4_grouped_gemm_out(kind, off, a, b, torch.bfloat16)
+        assert torch.equal(bf, f32.to(torch.bfloat16))
+    dyt, xt = rand_bf16((T, F), 9), x
+    dq = U.ufp4_rht_quantize(dyt, U.BLOCKS_ALONG_ROWS, True, 0x3C3C, group_offsets=off)
+    xtq = U.ufp4_rht_quantize(xt, U.BLOCKS_ALONG_ROWS, True, 0x3C3C, group_offsets=off)
+    f32 = U.ufp4_grouped_gemm(U.WGRAD, off, dq, xtq)
+    bf = U.ufp4_grouped_gemm_out(U.WGRAD, off, dq, xtq, torch.bfloat16)
+    assert torch.equal(bf, f32.to(torch.bfloat16)) and (bf[1] == 0).all()

@@ -37,11 +37,12 @@ ufp4_status check_pair(const ufp4_qtensor *a, const ufp4_qtensor *b) {
   return UFP4_OK;
 }
 
-ufp4_status dense_gemm(const ufp4_qtensor *a, const ufp4_qtensor *b, float *c, int64_t ldc,
-                       hipStream_t stream) {
+ufp4_status dense_gemm(const ufp4_qtensor *a, const ufp4_qtensor *b, void *c, int out_bf16,
+                       int64_t ldc, hipStream_t stream) {
   ufp4_status s = check_pair(a, b);
   if (s != UFP4_OK) return s;
   if (c == nullptr) return UFP4_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(c) & (out_bf16 ? 1u : 3u)) != 0) return UFP4_ERR_INVALID_ARG;
   if (ldc < b->rows) return UFP4_ERR_SHAPE;
   GemmArgs g{};
   g.a_codes = a->codes;
@@ -53,6 +54,7 @@ ufp4_status dense_gemm(const ufp4_qtensor *a, const ufp4_qtensor *b, float *c, i
   g.kpad = a->kpad;
   g.c = c;
   g.ldc = ldc;
+  g.out_bf16 = out_bf16;
   g.mode = 0;
   g.goff = nullptr;
   g.n_groups = 1;
@@ -219,27 +221,44 @@ ufp4_status ufp4_dequantize(const ufp4_qtensor *q, int32_t inverse_rht, float *o
 
 ufp4_status ufp4_gemm_fprop(const ufp4_qtensor *xq, const ufp4_qtensor *wq, float *y, int64_t ldy,
                             hipStream_t stream) {
-  return dense_gemm(xq, wq, y, ldy, stream);
+  return dense_gemm(xq, wq, y, 0, ldy, stream);
 }
 
 ufp4_status ufp4_gemm_dgrad(const ufp4_qtensor *dyq, const ufp4_qtensor *wtq, float *dx,
                             int64_t ldx, hipStream_t stream) {
-  return dense_gemm(dyq, wtq, dx, ldx, stream);
+  return dense_gemm(dyq, wtq, dx, 0, ldx, stream);
 }
 
 ufp4_status ufp4_gemm_wgrad(const ufp4_qtensor *dytq, const ufp4_qtensor *xtq, float *dw,
                             int64_t lddw, void *workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   if ((workspace == nullptr) != (workspace_bytes == 0)) return UFP4_ERR_INVALID_ARG;
-  return dense_gemm(dytq, xtq, dw, lddw, stream);
+  return dense_gemm(dytq, xtq, dw, 0, lddw, stream);
+}
+
+ufp4_status ufp4_gemm_out(int32_t kind, const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
+                          int32_t out_dtype, int64_t ldc, hipStream_t stream) {
+  if (kind < 0 || kind > 2) return UFP4_ERR_INVALID_ARG;
+  if (out_dtype != UFP4_OUT_F32 && out_dtype != UFP4_OUT_BF16) return UFP4_ERR_INVALID_ARG;
+  return dense_gemm(a, b, c, out_dtype == UFP4_OUT_BF16, ldc, stream);
 }
 
 ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
                               const ufp4_qtensor *a, const ufp4_qtensor *b, float *c, int64_t ldc,
                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if ((workspace == nullptr) != (workspace_bytes == 0)) return UFP4_ERR_INVALID_ARG;
+  return ufp4_grouped_gemm_out(kind, n_groups, d_group_offsets, a, b, c, UFP4_OUT_F32, ldc,
+                               stream);
+}
+
+ufp4_status ufp4_grouped_gemm_out(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
+                                  const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
+                                  int32_t out_dtype, int64_t ldc, hipStream_t stream) {
   if (kind < 0 || kind > 2) return UFP4_ERR_INVALID_ARG;
   if (d_group_offsets == nullptr || c == nullptr) return UFP4_ERR_INVALID_ARG;
-  if ((workspace == nullptr) != (workspace_bytes == 0)) return UFP4_ERR_INVALID_ARG;
+  if (out_dtype != UFP4_OUT_F32 && out_dtype != UFP4_OUT_BF16) return UFP4_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(c) & (out_dtype == UFP4_OUT_BF16 ? 1u : 3u)) != 0)
+    return UFP4_ERR_INVALID_ARG;
   if (n_groups < 1 || n_groups > kMaxGroupsApi) return UFP4_ERR_SHAPE;
   ufp4_status s = check_pair(a, b);
   if (s != UFP4_OK) return s;
@@ -251,6 +270,7 @@ ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_g
   g.kpad = a->kpad;
   g.c = c;
   g.ldc = ldc;
+  g.out_bf16 = out_dtype == UFP4_OUT_BF16;
   g.goff = d_group_offsets;
   g.n_groups = n_groups;
   g.grid = a->grid;

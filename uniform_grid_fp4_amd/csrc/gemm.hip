@@ -80,7 +80,7 @@ struct TileJob {
   int64_t a_row0, a_rows;   // A rows [a_row0, a_row0 + a_rows)
   int64_t b_row0, b_rows;
   int64_t kb0, kb1;         // block range [kb0, kb1)
-  float *c;                 // C element (0, 0) of the tile
+  int64_t c_off;            // element offset of C(0, 0) of the tile
 };
 
 // Per-thread staging registers of one stage.
@@ -241,13 +241,32 @@ struct Gemm {
     const int n0 = wn * kNT * 32 + l32;
     const int mrem = (int)job.a_rows - m0;
     const int nrem = (int)job.b_rows - n0;
-    float *cl = job.c + m0 * ldc + n0;
+    const int64_t off = job.c_off + m0 * ldc + n0;
+    if (g.out_bf16) {
+      // bf16 epilogue: the FP32 result rounded to nearest even (the bias
+      // 0x7FFF + lsb carries into the kept half exactly when the dropped half
+      // is above, or equal with an odd kept half; infinities stay infinite)
+      uint16_t *cl = static_cast<uint16_t *>(g.c) + off;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dm = 8 * (r >> 2) + (r & 3);
-        if (nt * 32 < nrem && dm < mrem) cl[dm * ldc + nt * 32] = acc[nt][r] * inv_g2;
+        for (int r = 0; r < 16; ++r) {
+          const int dm = 8 * (r >> 2) + (r & 3);
+          if (nt * 32 < nrem && dm < mrem) {
+            const uint32_t u = __float_as_uint(acc[nt][r] * inv_g2);
+            cl[dm * ldc + nt * 32] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+          }
+        }
+      }
+    } else {
+      float *cl = static_cast<float *>(g.c) + off;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dm = 8 * (r >> 2) + (r & 3);
+          if (nt * 32 < nrem && dm < mrem) cl[dm * ldc + nt * 32] = acc[nt][r] * inv_g2;
+        }
       }
     }
   }
@@ -376,7 +395,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       job.b_rows = min((int64_t)kBN, g.N - job.b_row0);
       job.kb0 = 0;
       job.kb1 = kblocks;
-      job.c = g.c + job.a_row0 * g.ldc + job.b_row0;
+      job.c_off = job.a_row0 * g.ldc + job.b_row0;
     } else if (MODE == 1) {
       int lo = 0, hi = g.n_groups;   // largest e with s_pre[e] <= t
       while (hi - lo > 1) {
@@ -393,7 +412,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       job.b_rows = min((int64_t)kBN, g.N - tn * kBN);
       job.kb0 = 0;
       job.kb1 = kblocks;
-      job.c = g.c + job.a_row0 * g.ldc + tn * kBN;
+      job.c_off = job.a_row0 * g.ldc + tn * kBN;
     } else {
       const int64_t per_group = tiles_m * tiles_n;
       const int64_t slot = t / per_group;
@@ -406,7 +425,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       job.b_rows = min((int64_t)kBN, g.N - job.b_row0);
       job.kb0 = min(s_pre[e] / 16, kblocks);
       job.kb1 = min(s_pre[e + 1] / 16, kblocks);
-      job.c = g.c + e * g.M * g.ldc + job.a_row0 * g.ldc + job.b_row0;
+      job.c_off = e * g.M * g.ldc + job.a_row0 * g.ldc + job.b_row0;
     }
     Gemm<GRID> gm(g, job);
     gm.run(stages);

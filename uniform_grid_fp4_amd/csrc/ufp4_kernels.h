@@ -89,8 +89,9 @@ struct GemmArgs {
   const uint8_t *b_codes;
   const float *b_scales;
   int64_t M, N, kpad;
-  float *c;
+  void *c;                  // FP32, or bf16 bit patterns when out_bf16
   int64_t ldc;
+  int out_bf16;             // 1: round the FP32 result to bf16 (nearest even)
   int mode;
   const int64_t *goff;
   int n_groups;

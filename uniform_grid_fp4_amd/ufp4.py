@@ -30,7 +30,7 @@ STATUS = {0: "UFP4_OK", -1: "UFP4_ERR_INVALID_ARG", -2: "UFP4_ERR_SHAPE",
 EXPORTS = ("ufp4_rht_quantize", "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop",
            "ufp4_gemm_dgrad", "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_workspace_size",
            "ufp4_status_string", "ufp4_stats_workspace_size", "ufp4_quant_stats",
-           "ufp4_output_stats")
+           "ufp4_output_stats", "ufp4_gemm_out", "ufp4_grouped_gemm_out")
 
 
 class UFP4Error(RuntimeError):
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.ufp4_gemm_dgrad.argtypes = [Q, Q, P, I64, P]
     L.ufp4_gemm_wgrad.argtypes = [Q, Q, P, I64, P, ctypes.c_size_t, P]
     L.ufp4_grouped_gemm.argtypes = [I32, I32, P, Q, Q, P, I64, P, ctypes.c_size_t, P]
+    L.ufp4_gemm_out.argtypes = [I32, Q, Q, P, I32, I64, P]
+    L.ufp4_grouped_gemm_out.argtypes = [I32, I32, P, Q, Q, P, I32, I64, P]
     L.ufp4_workspace_size.argtypes = [I32, I64, I64, I64, I32]
     L.ufp4_workspace_size.restype = ctypes.c_size_t
     L.ufp4_stats_workspace_size.argtypes = []
@@ -88,7 +90,7 @@ def lib() -> ctypes.CDLL:
     L.ufp4_status_string.restype = ctypes.c_char_p
     for f in ("ufp4_quant_stats", "ufp4_output_stats", "ufp4_rht_quantize",
               "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
-              "ufp4_gemm_wgrad", "ufp4_grouped_gemm"):
+              "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_gemm_out", "ufp4_grouped_gemm_out"):
         getattr(L, f).restype = ctypes.c_int32
     _lib = L
     return L
@@ -315,6 +317,43 @@ def ufp4_grouped_gemm(kind: int, group_offsets: torch.Tensor, a: Quantized, b: Q
                                  ctypes.byref(db), _ptr(out), ldc, ws, nbytes,
                                  _stream(out.device))
     _check(st, "ufp4_grouped_gemm")
+    return out
+
+
+OUT_F32, OUT_BF16 = 0, 1
+_OUT_CODE = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}
+
+
+def ufp4_gemm_out(kind: int, a: Quantized, b: Quantized, dtype=torch.bfloat16,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FPROP / DGRAD / WGRAD (kind 0 / 1 / 2) with a float32 or bfloat16
+    output written by the GEMM's epilogue."""
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=dtype, device=a.codes.device)
+    assert out.dtype in _OUT_CODE and out.stride(1) == 1
+    da, db = a.desc(), b.desc()
+    st = lib().ufp4_gemm_out(kind, ctypes.byref(da), ctypes.byref(db), _ptr(out),
+                             _OUT_CODE[out.dtype], out.stride(0), _stream(out.device))
+    _check(st, "ufp4_gemm_out")
+    return out
+
+
+def ufp4_grouped_gemm_out(kind: int, group_offsets: torch.Tensor, a: Quantized, b: Quantized,
+                          dtype=torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """ufp4_grouped_gemm with a float32 or bfloat16 output."""
+    n_groups = group_offsets.numel() - 1
+    if kind == WGRAD:
+        shape, ldc = (n_groups, a.rows, b.rows), b.rows
+    else:
+        shape, ldc = (a.rows, b.rows // n_groups), b.rows // n_groups
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=a.codes.device)
+    assert out.dtype in _OUT_CODE and out.is_contiguous()
+    da, db = a.desc(), b.desc()
+    st = lib().ufp4_grouped_gemm_out(kind, n_groups, _ptr(group_offsets), ctypes.byref(da),
+                                     ctypes.byref(db), _ptr(out), _OUT_CODE[out.dtype], ldc,
+                                     _stream(out.device))
+    _check(st, "ufp4_grouped_gemm_out")
     return out
 
 
