@@ -197,3 +197,37 @@ def test_dense_1p5b_dual_quantizer():
     ]
     for d, s in singles:
         assert torch.equal(d.codes, s.codes) and torch.equal(d.scales, s.scales)
+
+
+@pytest.mark.parametrize("make", [W.moe_7p9b, W.moe_124b], ids=["moe_7p9b", "moe_124b"])
+def test_moe_dual_quantizer_equals_single_axis(make):
+    """The expert layers' dual-axis quantizations (the bench's default path):
+    every output equals the single-axis call with the same options, whose
+    sampled rows the tests above check against the oracle."""
+    L = make(DEV)
+    mf, md, mw = L.masks
+    offd = torch.as_tensor(L.offsets, device=DEV)
+    C, R, S = U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS, U.BLOCKS_ALONG_ROWS_STACKED
+    print(f"[fullsize] {L.name} dual-axis quantizer", flush=True)
+    pairs = []
+    xq, xtq = U.ufp4_rht_quantize_dual(L.x, (True, mf, 0), (True, mw, 0), seed=SEED,
+                                       group_offsets=offd)
+    pairs += [(xq, U.ufp4_rht_quantize(L.x, C, True, mf, seed=SEED)),
+              (xtq, U.ufp4_rht_quantize(L.x, R, True, mw, seed=SEED, group_offsets=offd))]
+    del xq, xtq
+    wq, wtq = U.ufp4_rht_quantize_dual(L.w, (True, mf, 0), (True, md, 0), seed=SEED,
+                                       col_axis=S, n_groups=L.experts)
+    pairs += [(wq, U.ufp4_rht_quantize(L.w, C, True, mf, seed=SEED)),
+              (wtq, U.ufp4_rht_quantize(L.w, S, True, md, seed=SEED, n_groups=L.experts))]
+    for d, s in pairs:
+        assert torch.equal(d.codes, s.codes) and torch.equal(d.scales, s.scales)
+    del pairs, wq, wtq
+    dyq, dytq = U.ufp4_rht_quantize_dual(L.dy, (True, md, 0), (True, mw, 1), rnd=U.ROUND_SR,
+                                         seed=SEED, group_offsets=offd)
+    s1 = U.ufp4_rht_quantize(L.dy, C, True, md, rnd=U.ROUND_SR, seed=SEED, stream_id=0)
+    assert torch.equal(dyq.codes, s1.codes) and torch.equal(dyq.scales, s1.scales)
+    del s1, dyq
+    s2 = U.ufp4_rht_quantize(L.dy, R, True, mw, rnd=U.ROUND_SR, seed=SEED, stream_id=1,
+                             group_offsets=offd)
+    assert torch.equal(dytq.codes, s2.codes) and torch.equal(dytq.scales, s2.scales)
+    torch.cuda.empty_cache()
