@@ -83,13 +83,15 @@ def parse():
                     help="single: six single-axis quantizations per step; dual: three dual-axis "
                          "quantizations (one read of X, W and dY each, both operands out)")
     ap.add_argument("--workload", default="dense-1.5b",
-                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b", "copy", "q1-outputs"],
+                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b", "copy", "q1-outputs",
+                             "mfma-peak"],
                     help="dense-1.5b: the timed step (default); quant-sweep: the 2^28-element "
                          "quantizer sweep, one JSON line per case; moe-*: the expert layers "
                          "(grouped GEMMs), one JSON line; copy: a plain 1 GiB device copy, the "
                          "streaming ceiling and the calibration run of the HBM traffic "
                          "counters; q1-outputs: GEMM-output SQNR of each recipe against the "
-                         "unquantized product, one JSON line per GEMM")
+                         "unquantized product, one JSON line per GEMM; mfma-peak: measured "
+                         "rates of the candidate MFMA instructions")
     return ap.parse_args()
 
 
@@ -433,6 +435,53 @@ def q1_outputs(args):
         torch.cuda.empty_cache()
 
 
+MFMA_KINDS = ("v_mfma_f32_32x32x16_fp8_fp8", "v_mfma_i32_32x32x16_i8",
+              "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", "v_mfma_scale_f32_32x32x64_f8f6f4 (fp6)",
+              "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", "v_mfma_f32_32x32x16_bf16")
+# Useful 16-element block products per instruction when the per-16 FP32
+# scales have to be applied to each block's partial sum: a K = 16 instruction
+# yields one per output, a K = 64 one (zero-padded, or four blocks placed
+# block-diagonally along M) also one per output.
+MFMA_BLOCKS_PER_OUTPUT = (1, 1, 1, 1, 1, 1)
+
+
+def probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "uniform_grid_fp4_amd", "libufp4_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -m uniform_grid_fp4_amd.build")
+    L = ctypes.CDLL(path)
+    L.ufp4_probe_mfma_tflops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.ufp4_probe_mfma_tflops.restype = ctypes.c_double
+    L.ufp4_probe_mfma_flops.argtypes = [ctypes.c_int]
+    L.ufp4_probe_mfma_flops.restype = ctypes.c_double
+    return L
+
+
+def mfma_peak_tflops(kind: int) -> float:
+    """Sustained rate of one MFMA kind on this GPU (4096 workgroups x 4 waves
+    x 4 independent chains)."""
+    v = probe_lib().ufp4_probe_mfma_tflops(kind, 4096, 2000)
+    if v <= 0:
+        raise RuntimeError(f"MFMA probe failed ({v})")
+    return v
+
+
+def mfma_peaks(args):
+    """The candidate MFMA instructions for the block-scaled GEMM, measured:
+    the rate, and the rate of useful 16-element block products (the GEMM
+    needs each block's partial sum on its own to apply the FP32 scales)."""
+    import torch
+    assert torch.cuda.is_available()
+    L = probe_lib()
+    for kind, name in enumerate(MFMA_KINDS):
+        tf = mfma_peak_tflops(kind)
+        k = 16 if L.ufp4_probe_mfma_flops(kind) == 2.0 * 32 * 32 * 16 else 64
+        print(json.dumps({"workload": "mfma-peak", "instruction": name, "tflops": round(tf, 1),
+                          "k": k, "block_products_tflops_equiv": round(tf * 16 / k, 1)}),
+              flush=True)
+
+
 def copy_ceiling(args):
     """A plain contiguous 1 GiB device-to-device copy (torch's copy kernel):
     the streaming ceiling the quantizer is compared with, and the run whose
@@ -471,6 +520,8 @@ def main():
         return copy_ceiling(args)
     if args.workload == "q1-outputs":
         return q1_outputs(args)
+    if args.workload == "mfma-peak":
+        return mfma_peaks(args)
     import torch
     from uniform_grid_fp4_amd import ufp4 as U
     from uniform_grid_fp4_amd import workloads as W
@@ -509,6 +560,7 @@ def main():
     g_flop = 3 * st.gemm_flops()
     gemm_avg_ms = g_ms / 3
     gemm_tflops = st.gemm_flops() / (gemm_avg_ms * 1e-3) / 1e12
+    used_peak = mfma_peak_tflops(0)   # measured after the timed region
     step_tflops = g_flop / (ms_step * 1e-3) / 1e12
 
     out = {
@@ -536,6 +588,9 @@ def main():
                      "bytes_per_step": q_bytes},
         "gemm": {"tflops": round(gemm_tflops, 2),
                  "frac_fp8_mfma_peak": round(gemm_tflops / FP8_MFMA_PEAK_TFLOPS, 4),
+                 "used_instruction": MFMA_KINDS[0],
+                 "used_instruction_peak_tflops": round(used_peak, 1),
+                 "frac_used_instruction_peak": round(gemm_tflops / used_peak, 4),
                  "ms_per_step": round(g_ms, 4),
                  "per_call_ms": {n: round(dur[n], 4) for n in Step.GEMMS}},
         "roofline": {"kernel": ("ufp4::gemm_kernel<0, 1|2>" if isinstance(st, MoeStep)

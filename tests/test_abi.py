@@ -215,3 +215,13 @@ def test_gemm_out_validation():
     assert g(0, 0, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 1, 32, None) == -2
     assert g(1, 2, FAKE, ctypes.byref(ok), ctypes.byref(ok), ctypes.c_void_p(0x10001), 1, 32,
              None) == -1
+
+
+def test_probe_library_loads_and_rejects_bad_arguments():
+    import bench
+    L = bench.probe_lib()
+    assert L.ufp4_probe_mfma_flops(0) == 2 * 32 * 32 * 16
+    assert L.ufp4_probe_mfma_flops(4) == 2 * 32 * 32 * 64
+    assert L.ufp4_probe_mfma_flops(9) == 0
+    assert L.ufp4_probe_mfma_tflops(9, 1, 1) == -1.0      # rejected before any HIP call
+    assert L.ufp4_probe_mfma_tflops(0, 0, 1) == -1.0

@@ -14,6 +14,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libufp4.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "stats.hip"]
+# The bench's MFMA issue-rate probe: a separate library, not part of the ABI.
+PROBE_LIB = os.path.join(HERE, "libufp4_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 # -ffp-contract=off: no multiply-add fusion anywhere (the quantizer's two
 #   roundings r = RN(g/s), t = RN(y*r) must stay separate).
@@ -35,10 +38,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libufp4.so")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into uniform_grid_fp4_amd/libufp4.so."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(sources, out, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -49,7 +51,13 @@ def build(verbose: bool = False) -> str:
              if "packed-fp32-ops" not in ln and ln.strip()]
     if noise and verbose:
         print("\n".join(noise), file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source: libufp4.so and the probe library."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 
