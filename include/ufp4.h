@@ -142,7 +142,8 @@ typedef struct {
  *   0 < s < 2^-64 use y*2^64 and s*2^64 in that step (the stored scale is s).
  * Returns UFP4_OK, INVALID_ARG (null pointer, bad enum, codes/scales not
  *   16-byte aligned, reserved != 0), SHAPE (non-positive size, ld < n_cols,
- *   rows/kpad not what the call produces), HIP. */
+ *   rows/kpad not what the call produces), UNSUPPORTED (ALONG_ROWS or
+ *   ALONG_ROWS_STACKED with ld > 2^26 elements), HIP. */
 ufp4_status ufp4_rht_quantize(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols,
                               int64_t ld, int32_t axis, const int64_t *d_group_offsets,
                               int32_t n_groups, int32_t rht, uint32_t sign_mask,
@@ -201,7 +202,8 @@ ufp4_status ufp4_dequantize(const ufp4_qtensor *q, int32_t inverse_rht, float *o
  *   C[m, n] = sum_kb sa[m,kb] * sb[n,kb] * (sum_{k in kb} qa*qb) / g^2
  * over the operands' common kpad.  Operands must agree on k, kpad, grid, rht
  * and sign_mask (else UFP4_ERR_MISMATCH), which is what makes the rotation
- * cancel.  All three grids are accepted.
+ * cancel.  All three grids are accepted; kpad > 2^24 returns
+ * UFP4_ERR_UNSUPPORTED.
  *   FPROP: A = X  [T, H] (blocks along H), B = W   [F, H]  -> Y  [T, F]
  *   DGRAD: A = dY [T, F] (blocks along F), B = W^T [H, F] (W quantized with
  *          ALONG_ROWS) -> dX [T, H]

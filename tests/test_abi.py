@@ -225,3 +225,10 @@ def test_probe_library_loads_and_rejects_bad_arguments():
     assert L.ufp4_probe_mfma_flops(9) == 0
     assert L.ufp4_probe_mfma_tflops(9, 1, 1) == -1.0      # rejected before any HIP call
     assert L.ufp4_probe_mfma_tflops(0, 0, 1) == -1.0
+
+
+def test_size_limits_of_32_bit_offsets():
+    # column-wise quantization of rows longer than 2^26 elements, GEMM K beyond 2^24
+    assert quant(axis=1, ld=(1 << 26) + 2, out=fake_desc(rows=32, kpad=32)) == -4
+    big = fake_desc(k=(1 << 24) + 16, kpad=(1 << 24) + 16)
+    assert gemm(U.lib().ufp4_gemm_fprop, big, big) == -4

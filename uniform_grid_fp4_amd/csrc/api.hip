@@ -26,11 +26,18 @@ ufp4_status check_qtensor(const ufp4_qtensor *q) {
   return UFP4_OK;
 }
 
+// Size limits of the kernels' 32-bit buffer offsets: a GEMM tile's operand
+// panel (128 rows x kpad/2 bytes) and a column-wise quantizer block (16 rows
+// of ld elements) must stay below 2^31 bytes.
+constexpr int64_t kMaxKpad = int64_t(1) << 24;
+constexpr int64_t kMaxColumnLd = int64_t(1) << 26;
+
 ufp4_status check_pair(const ufp4_qtensor *a, const ufp4_qtensor *b) {
   ufp4_status s = check_qtensor(a);
   if (s != UFP4_OK) return s;
   s = check_qtensor(b);
   if (s != UFP4_OK) return s;
+  if (a->kpad > kMaxKpad) return UFP4_ERR_UNSUPPORTED;
   if (a->k != b->k || a->kpad != b->kpad || a->grid != b->grid || a->rht != b->rht ||
       (a->rht && ((a->sign_mask ^ b->sign_mask) & 0xFFFFu) != 0))
     return UFP4_ERR_MISMATCH;
@@ -81,6 +88,7 @@ ufp4_status check_quant(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, 
   if (rht != 0 && rht != 1) return UFP4_ERR_INVALID_ARG;
   if (sign_mask > 0xFFFFu) return UFP4_ERR_INVALID_ARG;
   if (n_rows <= 0 || n_cols <= 0 || ld < n_cols) return UFP4_ERR_SHAPE;
+  if (axis != UFP4_BLOCKS_ALONG_COLS && ld > kMaxColumnLd) return UFP4_ERR_UNSUPPORTED;
   if (axis == UFP4_BLOCKS_ALONG_COLS && (d_group_offsets != nullptr || n_groups != 0))
     return UFP4_ERR_INVALID_ARG;
   if (axis == UFP4_BLOCKS_ALONG_ROWS) {
