@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "ufp4_device.h"
 #include "ufp4_kernels.h"
 
@@ -51,8 +53,10 @@ __device__ __forceinline__ void quantize_store(const uint4 a0, const uint4 a1, i
   uint32_t w0, w1;
   float s;
   quantize_block<GRID, RND, RHT>(v, (uint64_t)b * 16u, seed_lo, seed_hi, stream_id, w0, w1, s);
-  *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(w0, w1);
-  scales[b] = s;
+  // streaming stores: the outputs are read back only by a later kernel
+  __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t *>(codes + b * 8));
+  __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t *>(codes + b * 8) + 1);
+  __builtin_nontemporal_store(s, scales + b);
 }
 
 template <int GRID, int RND, bool RHT>
@@ -636,13 +640,33 @@ static int grid_for(int64_t work_items, int per_block, int max_blocks) {
   return (int)b;
 }
 
+// Compute units of the current device, queried once per device.
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int GRID, int RND, bool RHT>
 static hipError_t launch_rows_t(const QuantArgs &a, hipStream_t st) {
   const int64_t kblocks = a.kpad / 16;
   const bool aligned = (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
   if (aligned && a.ld == a.n_cols && a.n_cols % 16 == 0) {
     const int64_t nblk = a.n_rows * kblocks;
-    const int blocks = grid_for(nblk, 256, 256 * 8);
+    // A persistent-style grid: with round-to-nearest the loop is bound by
+    // HBM and two workgroups per CU keep enough loads in flight; the Philox
+    // draws of stochastic rounding make it ALU-heavier, so it gets four.
+    const int per_cu = RND == kRoundSR ? 4 : 2;
+    const int blocks = grid_for(nblk, 256, per_cu * device_cus());
     hipLaunchKernelGGL((quant_rows_contig_kernel<GRID, RND, RHT>), dim3(blocks), dim3(256), 0, st,
                        a.x, nblk, a.codes, a.scales, a.sign_mask, a.seed_lo, a.seed_hi,
                        a.stream_id);
