@@ -30,15 +30,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA
-# The GEMM is bound by its per-block FP32 rescale on the vector ALU: two VALU
-# operations (a multiply and an FMA) per output per 16-element block, i.e.
-# 2 ops per 16 MACs.  Non-packed FP32 VALU issue on gfx950: a wave64
-# instruction every 2 cycles per SIMD, i.e. 256 CU x 4 SIMD x 32 lanes x
-# 2.4 GHz = 78.64e12 lane-ops/s (the same unit count gives the published
-# 157.3 TFLOP/s FP32 vector FMA peak).  GEMM ceiling:
-# 78.64e12 * 16 MAC / 2 ops * 2 FLOP/MAC = 1258.3 TFLOP/s.
-VALU_LANE_OPS = 256 * 4 * 32 * 2.4e9
-GEMM_ALU_PEAK_TFLOPS = VALU_LANE_OPS * 16.0 / 2.0 * 2.0 / 1e12
+# The GEMM's work per unit of one 32x32 output tile and one 16-element block
+# (32768 FLOP): one v_mfma_f32_32x32x16_fp8_fp8 for the exact block product
+# (32 matrix-core cycles), half of one v_mfma_f32_32x32x1_2b_f32 for the FP32
+# scale products of a 32 x 64 wave tile (64 cycles for both 32x32 halves) and
+# 16 vector FMAs acc += S * P (4 issue cycles per wave64 instruction).  The
+# matrix core and the vector ALU each need 64 cycles per unit, so the ceiling
+# of this instruction mix is 32768 FLOP / 64 cycles x 1024 SIMDs x 2.4 GHz =
+# 1258.3 TFLOP/s (a quarter of the 5.0 PFLOP/s FP8 MFMA peak).
+SIMDS = 256 * 4
+GEMM_UNIT_CYCLES = 64
+GEMM_PIPE_PEAK_TFLOPS = 32 * 32 * 16 * 2 / GEMM_UNIT_CYCLES * SIMDS * 2.4e9 / 1e12
 BYTES_PER_QUANT_ELEM = 2.0 + 0.5 + 0.25
 BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 
@@ -48,8 +50,8 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # of a plain 1 GiB device copy.  The figures hold for the GEMM source whose
 # SHA-256 is recorded with them; any other source reports null.
 GEMM_TRAFFIC = {
-    "dense-1.5B-fc1": {"sha256": "1c74a91a666c2fa32a4874cfed19e4f2782838b17aacee88f923e39346369453",
-                       "bytes_per_launch": 392686302},
+    "dense-1.5B-fc1": {"sha256": "d640fabaa819bb8a8ecee99a9f8016c1a153aa16870f1de6398789cf48edb92a",
+                       "bytes_per_launch": 388109489},
 }
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
@@ -595,10 +597,10 @@ def main():
                  "per_call_ms": {n: round(dur[n], 4) for n in Step.GEMMS}},
         "roofline": {"kernel": ("ufp4::gemm_kernel<0, 1|2>" if isinstance(st, MoeStep)
                                 else "ufp4::gemm_kernel<0, 0>"),
-                     "bound": "alu",
-                     "achieved": round(gemm_tflops, 2), "peak": round(GEMM_ALU_PEAK_TFLOPS, 1),
+                     "bound": "mfma",
+                     "achieved": round(gemm_tflops, 2), "peak": round(GEMM_PIPE_PEAK_TFLOPS, 1),
                      "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / GEMM_ALU_PEAK_TFLOPS, 4),
+                     "frac": round(gemm_tflops / GEMM_PIPE_PEAK_TFLOPS, 4),
                      "traffic": gemm_traffic(L.name)},
     }
     if not args.no_cpu_baseline and args.workload == "dense-1.5b":

@@ -11,25 +11,31 @@
 // Design for gfx950: every grid level is an exact FP8 E4M3 value (uniform:
 // 0..7; E2M1 doubled: 0,1,2,3,4,6,8,12), so one v_mfma_f32_32x32x16_fp8_fp8
 // per 16-element block yields P_kb exactly in FP32 (|P| <= 16*144).  The
-// per-block rescale is an FP32 multiply and an FMA per output on the vector
-// ALU -- two VALU operations per 16 MACs -- and that, not the matrix core,
-// bounds this kernel; MFMAs of one wave overlap the rescale of the other wave
-// on the same SIMD.  Nibbles are expanded to FP8 (v_perm_b32 look-up) once per
-// workgroup while staging into LDS, so the waves read ready MFMA operands.
+// scale products sa[m,kb]*sb[n,kb] of a wave's 32 x 64 outputs are one FP32
+// outer product, computed by v_mfma_f32_32x32x1_2b_f32 (K = 1, the A column
+// broadcast to both 32-column blocks): an exact product rounded once, the
+// same value as an FP32 multiply, in the same lane/register layout as P.
+// What remains on the vector ALU is one FMA per output per block,
+// acc += S * P.  Vector instructions (4 issue cycles each) and the waits on
+// MFMA results bound this kernel, not the matrix core.  Nibbles are expanded
+// to FP8 (v_perm_b32 look-up) once per workgroup while staging into LDS, so
+// the waves read ready MFMA operands.
 //
 // Tiling: 512 threads = 8 waves, 128 x 128 output tile; the waves form a
 // 4 x 2 grid and wave (wm, wn) owns rows [32wm, 32wm+32) x columns
-// [64wn, 64wn+64) = two 32x32 MFMA tiles sharing one A fragment and one set
-// of 16 row scales per block.  The kernel is built for 4 waves per SIMD (at
-// most 128 VGPRs, two workgroups per CU): the rescale issues one VALU
-// instruction per wave only every ~5 cycles, so a SIMD needs several waves
-// ready to keep its vector ALU busy while others wait on MFMA results, LDS
-// or the barrier.  K advances 64 (4 blocks) per LDS stage, double-buffered:
-// the global loads of stage s+1 are in flight while stage s is computed, and
-// there is one barrier per stage.  Operands are read with buffer loads whose
+// [64wn, 64wn+64) = two 32x32 MFMA tiles sharing one A fragment and one
+// scale outer product per block.  The kernel is built for 4 waves per SIMD
+// (at most 128 VGPRs, two workgroups per CU) so that a SIMD has other waves
+// to issue while one waits on MFMA results, LDS or the barrier.  K advances
+// 64 (4 blocks) per LDS stage, double-buffered: the global loads of stage
+// s+1 are in flight while stage s is computed, and there is one barrier per
+// stage; the stage loop is unrolled by two so each half addresses its LDS
+// buffer with constant offsets.  Operands are read with buffer loads whose
 // range check returns zero past the tile's rows, so ragged edges need no
-// branches.  Tiles are assigned XCD-major: the 8 XCDs each walk a contiguous
-// range of tiles, so a row panel of A stays in one L2.
+// branches; full stages carry the stage offset in the scalar offset, and
+// only the last, partial stage tests each lane's block against the K range.
+// Tiles are assigned XCD-major: the 8 XCDs each walk a contiguous range of
+// tiles, so a row panel of A stays in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +45,7 @@
 namespace ufp4 {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx32 __attribute__((ext_vector_type(32)));
 
 constexpr int kThreads = 512;
 constexpr int kWavesM = 4;                    // waves along M
@@ -52,6 +59,7 @@ constexpr int kAItems = kBM * kSB / kThreads; // (row, block) items per thread: 
 constexpr int kBItems = kBN * kSB / kThreads; // 1
 static_assert(kAItems * kThreads == kBM * kSB && kBItems * kThreads == kBN * kSB, "staging");
 static_assert((1 << kSBLog) == kSB, "kSBLog");
+static_assert(kAItems == 1 && kBItems == 1, "one A and one B staging item per thread");
 constexpr int kMaxGemmGroups = 1024;
 constexpr int kXcds = 8;
 
@@ -101,67 +109,59 @@ struct Gemm {
   const GemmArgs &g;
   TileJob job;
   __amdgpu_buffer_rsrc_t ra_q, ra_s, rb_q, rb_s;
-  int64_t kblocks;
+  int nkb;     // blocks in [kb0, kb1)
+  int oq, os;  // this thread's (row, block) item at stage 0: code and scale byte offsets
 
   __device__ Gemm(const GemmArgs &args, const TileJob &j) : g(args), job(j) {
-    kblocks = g.kpad / 16;
+    const int64_t kblocks = g.kpad / 16;
     // Resources start at the tile's first row, so 32-bit offsets suffice and
     // rows past the tile read as zero.
     ra_q = make_rsrc(g.a_codes + job.a_row0 * (g.kpad / 2), job.a_rows * (g.kpad / 2));
     ra_s = make_rsrc(g.a_scales + job.a_row0 * kblocks, job.a_rows * kblocks * 4);
     rb_q = make_rsrc(g.b_codes + job.b_row0 * (g.kpad / 2), job.b_rows * (g.kpad / 2));
     rb_s = make_rsrc(g.b_scales + job.b_row0 * kblocks, job.b_rows * kblocks * 4);
+    nkb = (int)(job.kb1 - job.kb0);
+    const int row = threadIdx.x >> kSBLog, blk = threadIdx.x & (kSB - 1);
+    oq = (int)(row * (g.kpad / 2) + (job.kb0 + blk) * 8);
+    os = (int)((row * kblocks + job.kb0 + blk) * 4);
   }
 
-  __device__ __forceinline__ void load(Regs &r, int64_t kb) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < kAItems; ++j) {
-      const int i = tid + kThreads * j;
-      const int row = i >> kSBLog, blk = i & (kSB - 1);
-      const bool ok = kb + blk < job.kb1;
-      const int oq = ok ? (int)(row * (g.kpad / 2) + (kb + blk) * 8) : 0x7FFFFFF8;
-      const int os = ok ? (int)((row * kblocks + kb + blk) * 4) : 0x7FFFFFF8;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra_q, oq, 0, 0);
-      r.aq[j] = make_uint2(v[0], v[1]);
-      r.as[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra_s, os, 0, 0));
+  // Global loads of stage st (blocks kb0 + st*kSB ...).  Full stages put the
+  // stage offset in the scalar offset; only the last, partial stage needs the
+  // per-lane range test (offsets past the resource read as zero).
+  __device__ __forceinline__ void load(Regs &r, int st) const {
+    const int kbs = st * kSB;
+    int vq = oq, vs = os, sq = kbs * 8, ss = kbs * 4;
+    if (kbs + kSB > nkb) {
+      const bool ok = kbs + (int)(threadIdx.x & (kSB - 1)) < nkb;
+      vq = ok ? oq + sq : 0x7FFFFFF8;
+      vs = ok ? os + ss : 0x7FFFFFF8;
+      sq = 0;
+      ss = 0;
     }
-#pragma unroll
-    for (int j = 0; j < kBItems; ++j) {
-      const int i = tid + kThreads * j;
-      const int row = i >> kSBLog, blk = i & (kSB - 1);
-      const bool ok = kb + blk < job.kb1;
-      const int oq = ok ? (int)(row * (g.kpad / 2) + (kb + blk) * 8) : 0x7FFFFFF8;
-      const int os = ok ? (int)((row * kblocks + kb + blk) * 4) : 0x7FFFFFF8;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rb_q, oq, 0, 0);
-      r.bq[j] = make_uint2(v[0], v[1]);
-      r.bs[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_s, os, 0, 0));
-    }
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(ra_q, vq, sq, 0);
+    r.aq[0] = make_uint2(a[0], a[1]);
+    r.as[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra_s, vs, ss, 0));
+    const auto b = __builtin_amdgcn_raw_buffer_load_b64(rb_q, vq, sq, 0);
+    r.bq[0] = make_uint2(b[0], b[1]);
+    r.bs[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_s, vs, ss, 0));
   }
 
   __device__ __forceinline__ static void store(const Regs &r, Stage &s) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < kAItems; ++j) {
-      const int i = tid + kThreads * j;
-      const int row = i >> kSBLog, blk = i & (kSB - 1);
-      uint2 *dst = reinterpret_cast<uint2 *>(s.a + row * kRowBytes + blk * 16);
-      dst[0] = nib8_to_fp8<GRID>(r.aq[j].x);
-      dst[1] = nib8_to_fp8<GRID>(r.aq[j].y);
-      s.sa[blk * kBM + row] = r.as[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kBItems; ++j) {
-      const int i = tid + kThreads * j;
-      const int row = i >> kSBLog, blk = i & (kSB - 1);
-      uint2 *dst = reinterpret_cast<uint2 *>(s.b + row * kRowBytes + blk * 16);
-      dst[0] = nib8_to_fp8<GRID>(r.bq[j].x);
-      dst[1] = nib8_to_fp8<GRID>(r.bq[j].y);
-      s.sb[blk * kBN + row] = r.bs[j];
-    }
+    const int row = threadIdx.x >> kSBLog, blk = threadIdx.x & (kSB - 1);
+    uint2 *da = reinterpret_cast<uint2 *>(s.a + row * kRowBytes + blk * 16);
+    da[0] = nib8_to_fp8<GRID>(r.aq[0].x);
+    da[1] = nib8_to_fp8<GRID>(r.aq[0].y);
+    s.sa[blk * kBM + row] = r.as[0];
+    uint2 *db = reinterpret_cast<uint2 *>(s.b + row * kRowBytes + blk * 16);
+    db[0] = nib8_to_fp8<GRID>(r.bq[0].x);
+    db[1] = nib8_to_fp8<GRID>(r.bq[0].y);
+    s.sb[blk * kBN + row] = r.bs[0];
   }
 
-  // One stage: kSB blocks x (2 MFMA + 32 scale products + 32 FMAs) per wave.
+  // One stage: per block, the two 32x32 block products P (FP8 MFMA) and the
+  // scale products S = sa x sb of the wave's 32 x 64 outputs (one FP32
+  // outer-product MFMA), then acc += S * P with one FMA per output.
   __device__ __forceinline__ static void compute(const Stage &s, floatx16 (&acc)[kNT]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -171,33 +171,24 @@ struct Gemm {
     floatx16 zero;
 #pragma unroll
     for (int r = 0; r < 16; ++r) zero[r] = 0.0f;
+    floatx32 zero32;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) zero32[r] = 0.0f;
     const uint8_t *pa = s.a + (wm * 32 + l32) * kRowBytes + 8 * half;
     const uint8_t *pb = s.b + (wn * 32 * kNT + l32) * kRowBytes + 8 * half;
-    const float *psa = s.sa + wm * 32 + 4 * half;
-    const float *psb = s.sb + wn * 32 * kNT + l32;
+    const float *psa = s.sa + wm * 32 + l32;
+    const float *psb = s.sb + wn * 32 * kNT + lane;
 #pragma unroll 1
     for (int b = 0; b < kSB; ++b) {
       const long af = *reinterpret_cast<const long *>(pa + b * 16);
-      floatx16 p[kNT];
+      const floatx32 S = __builtin_amdgcn_mfma_f32_32x32x1f32(psa[b * kBM], psb[b * kBN], zero32,
+                                                              1, 0, 0);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         const long bf = *reinterpret_cast<const long *>(pb + nt * 32 * kRowBytes + b * 16);
-        p[nt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af, bf, zero, 0, 0, 0);
-      }
-      float sa[16];
+        const floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af, bf, zero, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 v = *reinterpret_cast<const float4 *>(psa + b * kBM + 8 * j);
-        sa[4 * j + 0] = v.x;
-        sa[4 * j + 1] = v.y;
-        sa[4 * j + 2] = v.z;
-        sa[4 * j + 3] = v.w;
-      }
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const float sb = psb[b * kBN + nt * 32];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nt][r] = fmaf(sa[r] * sb, p[nt][r], acc[nt][r]);
+        for (int r = 0; r < 16; ++r) acc[nt][r] = fmaf(S[16 * nt + r], p[r], acc[nt][r]);
       }
     }
   }
@@ -209,17 +200,23 @@ struct Gemm {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
-    const int64_t nstages = (job.kb1 - job.kb0 + kSB - 1) / kSB;
-    if (nstages > 0) {
+    const int nst = (nkb + kSB - 1) / kSB;
+    if (nst > 0) {
       Regs r;
-      load(r, job.kb0);
+      load(r, 0);
       store(r, stages[0]);
       __syncthreads();
-      for (int64_t st = 0; st < nstages; ++st) {
-        const bool more = st + 1 < nstages;
-        if (more) load(r, job.kb0 + (st + 1) * kSB);
-        compute(stages[st & 1], acc);
-        if (more) store(r, stages[(st + 1) & 1]);
+      // unrolled by two so that each half addresses its LDS buffer with
+      // constant offsets
+      for (int st = 0; st < nst; st += 2) {
+        if (st + 1 < nst) load(r, st + 1);
+        compute(stages[0], acc);
+        if (st + 1 < nst) store(r, stages[1]);
+        __syncthreads();
+        if (st + 1 >= nst) break;
+        if (st + 2 < nst) load(r, st + 2);
+        compute(stages[1], acc);
+        if (st + 2 < nst) store(r, stages[0]);
         __syncthreads();
       }
     }
