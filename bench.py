@@ -50,8 +50,8 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # of a plain 1 GiB device copy.  The figures hold for the GEMM source whose
 # SHA-256 is recorded with them; any other source reports null.
 GEMM_TRAFFIC = {
-    "dense-1.5B-fc1": {"sha256": "d640fabaa819bb8a8ecee99a9f8016c1a153aa16870f1de6398789cf48edb92a",
-                       "bytes_per_launch": 388109489},
+    "dense-1.5B-fc1": {"sha256": "514b89b81a574c806f54d680b525e878ab01e12939a8e985caf6160b5b240ef1",
+                       "bytes_per_launch": 390355678},
 }
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
@@ -439,12 +439,16 @@ def q1_outputs(args):
 
 MFMA_KINDS = ("v_mfma_f32_32x32x16_fp8_fp8", "v_mfma_i32_32x32x16_i8",
               "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", "v_mfma_scale_f32_32x32x64_f8f6f4 (fp6)",
-              "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", "v_mfma_f32_32x32x16_bf16")
-# Useful 16-element block products per instruction when the per-16 FP32
-# scales have to be applied to each block's partial sum: a K = 16 instruction
-# yields one per output, a K = 64 one (zero-padded, or four blocks placed
-# block-diagonally along M) also one per output.
-MFMA_BLOCKS_PER_OUTPUT = (1, 1, 1, 1, 1, 1)
+              "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", "v_mfma_f32_32x32x16_bf16",
+              "v_mfma_f32_32x32x1_2b_f32")
+# The block-product candidates (kinds 0-5): a K = 16 instruction yields one
+# useful 16-element block product per output, and so does a K = 64 one
+# (zero-padded, or four blocks placed block-diagonally along M), since the
+# per-16 FP32 scales must be applied to each block's partial sum.  Kind 6 is
+# the FP32 outer product the GEMM uses for the scale products.
+MFMA_BLOCK_PRODUCT_KINDS = 6
+MIX_MODES = ("2 FP8 MFMA + 1 FP32 outer-product MFMA + 32 FMA", "32 FMA only",
+             "2 FP8 MFMA + 1 FP32 outer-product MFMA only")
 
 
 def probe_lib():
@@ -457,6 +461,8 @@ def probe_lib():
     L.ufp4_probe_mfma_tflops.restype = ctypes.c_double
     L.ufp4_probe_mfma_flops.argtypes = [ctypes.c_int]
     L.ufp4_probe_mfma_flops.restype = ctypes.c_double
+    L.ufp4_probe_mix_ms.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.ufp4_probe_mix_ms.restype = ctypes.c_double
     return L
 
 
@@ -469,6 +475,19 @@ def mfma_peak_tflops(kind: int) -> float:
     return v
 
 
+def instruction_mix_tflops() -> float:
+    """Rate of the GEMM's per-block instruction mix run on its own (two FP8
+    MFMAs, one FP32 outer-product MFMA and 32 FMAs per wave-iteration = two
+    32x32x16 units, 4 waves per SIMD, no memory traffic): the ceiling this
+    instruction mix reaches on this GPU, given how little matrix-core and
+    vector work overlap on one SIMD."""
+    wgs, reps = 4096, 2000
+    ms = probe_lib().ufp4_probe_mix_ms(0, wgs, reps)
+    if ms <= 0:
+        raise RuntimeError(f"mix probe failed ({ms})")
+    return wgs * 4 * reps * 2 * (2.0 * 32 * 32 * 16) / (ms * 1e-3) / 1e12
+
+
 def mfma_peaks(args):
     """The candidate MFMA instructions for the block-scaled GEMM, measured:
     the rate, and the rate of useful 16-element block products (the GEMM
@@ -478,10 +497,29 @@ def mfma_peaks(args):
     L = probe_lib()
     for kind, name in enumerate(MFMA_KINDS):
         tf = mfma_peak_tflops(kind)
-        k = 16 if L.ufp4_probe_mfma_flops(kind) == 2.0 * 32 * 32 * 16 else 64
-        print(json.dumps({"workload": "mfma-peak", "instruction": name, "tflops": round(tf, 1),
-                          "k": k, "block_products_tflops_equiv": round(tf * 16 / k, 1)}),
-              flush=True)
+        flops = L.ufp4_probe_mfma_flops(kind)
+        line = {"workload": "mfma-peak", "instruction": name, "tflops": round(tf, 1),
+                "cycles_per_instruction_2p4ghz": round(flops / (tf * 1e12 / SIMDS / 2.4e9), 1)}
+        if kind < MFMA_BLOCK_PRODUCT_KINDS:
+            k = 16 if flops == 2.0 * 32 * 32 * 16 else 64
+            line.update(k=k, block_products_tflops_equiv=round(tf * 16 / k, 1))
+        print(json.dumps(line), flush=True)
+    # Co-execution: the GEMM's per-block mix of one wave against its parts,
+    # in SIMD cycles per wave-iteration at the nominal 2.4 GHz (4096
+    # workgroups x 4 waves = 4 waves per SIMD).  If matrix-core and vector
+    # work overlapped, the mix would take the larger of its parts; if they
+    # serialised, their sum.
+    wgs, reps = 4096, 2000
+    cyc = []
+    for mode, name in enumerate(MIX_MODES):
+        ms = L.ufp4_probe_mix_ms(mode, wgs, reps)
+        if ms <= 0:
+            raise RuntimeError(f"mix probe failed ({ms})")
+        cyc.append(ms * 1e-3 * SIMDS * 2.4e9 / (wgs * 4 * reps))
+        print(json.dumps({"workload": "mfma-vs-valu", "loop": name,
+                          "simd_cycles_per_wave_iteration": round(cyc[-1], 1)}), flush=True)
+    print(json.dumps({"workload": "mfma-vs-valu", "mix_over_max_of_parts": round(cyc[0] / max(cyc[1:]), 3),
+                      "mix_over_sum_of_parts": round(cyc[0] / (cyc[1] + cyc[2]), 3)}), flush=True)
 
 
 def copy_ceiling(args):
@@ -563,6 +601,7 @@ def main():
     gemm_avg_ms = g_ms / 3
     gemm_tflops = st.gemm_flops() / (gemm_avg_ms * 1e-3) / 1e12
     used_peak = mfma_peak_tflops(0)   # measured after the timed region
+    mix_peak = instruction_mix_tflops()
     step_tflops = g_flop / (ms_step * 1e-3) / 1e12
 
     out = {
@@ -593,6 +632,8 @@ def main():
                  "used_instruction": MFMA_KINDS[0],
                  "used_instruction_peak_tflops": round(used_peak, 1),
                  "frac_used_instruction_peak": round(gemm_tflops / used_peak, 4),
+                 "instruction_mix_tflops": round(mix_peak, 1),
+                 "frac_instruction_mix": round(gemm_tflops / mix_peak, 4),
                  "ms_per_step": round(g_ms, 4),
                  "per_call_ms": {n: round(dur[n], 4) for n in Step.GEMMS}},
         "roofline": {"kernel": ("ufp4::gemm_kernel<0, 1|2>" if isinstance(st, MoeStep)

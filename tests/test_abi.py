@@ -222,9 +222,12 @@ def test_probe_library_loads_and_rejects_bad_arguments():
     L = bench.probe_lib()
     assert L.ufp4_probe_mfma_flops(0) == 2 * 32 * 32 * 16
     assert L.ufp4_probe_mfma_flops(4) == 2 * 32 * 32 * 64
+    assert L.ufp4_probe_mfma_flops(6) == 2 * 32 * 32 * 2   # FP32 outer product, two blocks
     assert L.ufp4_probe_mfma_flops(9) == 0
     assert L.ufp4_probe_mfma_tflops(9, 1, 1) == -1.0      # rejected before any HIP call
     assert L.ufp4_probe_mfma_tflops(0, 0, 1) == -1.0
+    assert L.ufp4_probe_mix_ms(3, 1, 1) == -1.0
+    assert L.ufp4_probe_mix_ms(0, 1, 0) == -1.0
 
 
 def test_size_limits_of_32_bit_offsets():

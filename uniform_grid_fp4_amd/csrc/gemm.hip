@@ -178,18 +178,25 @@ struct Gemm {
     const uint8_t *pb = s.b + (wn * 32 * kNT + l32) * kRowBytes + 8 * half;
     const float *psa = s.sa + wm * 32 + l32;
     const float *psb = s.sb + wn * 32 * kNT + lane;
-#pragma unroll 1
+#pragma unroll
     for (int b = 0; b < kSB; ++b) {
-      const long af = *reinterpret_cast<const long *>(pa + b * 16);
-      const floatx32 S = __builtin_amdgcn_mfma_f32_32x32x1f32(psa[b * kBM], psb[b * kBN], zero32,
-                                                              1, 0, 0);
+      long af = *reinterpret_cast<const long *>(pa + b * 16);
+      long bf0 = *reinterpret_cast<const long *>(pb + b * 16);
+      long bf1 = *reinterpret_cast<const long *>(pb + 32 * kRowBytes + b * 16);
+      float a1 = psa[b * kBM];
+      float b1 = psb[b * kBN];
+      // this block's MFMAs may not start before the previous block's FMAs
+      // are done (keeps the unrolled blocks from holding several blocks'
+      // products in registers); the LDS reads above may run ahead
+      asm volatile("" : "+v"(af), "+v"(bf0), "+v"(bf1), "+v"(a1), "+v"(b1)
+                   : "v"(acc[0]), "v"(acc[1]));
+      const floatx32 S = __builtin_amdgcn_mfma_f32_32x32x1f32(a1, b1, zero32, 1, 0, 0);
+      const floatx16 p0 = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af, bf0, zero, 0, 0, 0);
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const long bf = *reinterpret_cast<const long *>(pb + nt * 32 * kRowBytes + b * 16);
-        const floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af, bf, zero, 0, 0, 0);
+      for (int r = 0; r < 16; ++r) acc[0][r] = fmaf(S[r], p0[r], acc[0][r]);
+      const floatx16 p1 = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af, bf1, zero, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nt][r] = fmaf(S[16 * nt + r], p[r], acc[nt][r]);
-      }
+      for (int r = 0; r < 16; ++r) acc[1][r] = fmaf(S[16 + r], p1[r], acc[1][r]);
     }
   }
 
