@@ -50,8 +50,8 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # of a plain 1 GiB device copy.  The figures hold for the GEMM source whose
 # SHA-256 is recorded with them; any other source reports null.
 GEMM_TRAFFIC = {
-    "dense-1.5B-fc1": {"sha256": "514b89b81a574c806f54d680b525e878ab01e12939a8e985caf6160b5b240ef1",
-                       "bytes_per_launch": 390355678},
+    "dense-1.5B-fc1": {"sha256": "5bf9b9e659db18413c763ca5ad6c20ccd5379845ccbc4c8cd1ea4b67255df148",
+                       "bytes_per_launch": 390316948},
 }
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
@@ -440,12 +440,14 @@ def q1_outputs(args):
 MFMA_KINDS = ("v_mfma_f32_32x32x16_fp8_fp8", "v_mfma_i32_32x32x16_i8",
               "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", "v_mfma_scale_f32_32x32x64_f8f6f4 (fp6)",
               "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", "v_mfma_f32_32x32x16_bf16",
-              "v_mfma_f32_32x32x1_2b_f32")
+              "v_mfma_f32_32x32x1_2b_f32", "v_mfma_f32_32x32x8_bf16")
 # The block-product candidates (kinds 0-5): a K = 16 instruction yields one
 # useful 16-element block product per output, and so does a K = 64 one
 # (zero-padded, or four blocks placed block-diagonally along M), since the
-# per-16 FP32 scales must be applied to each block's partial sum.  Kind 6 is
-# the FP32 outer product the GEMM uses for the scale products.
+# per-16 FP32 scales must be applied to each block's partial sum.  Kinds 6
+# and 7 are candidates for the scale products: the FP32 outer product the
+# GEMM uses, and the K = 8 bf16 form a three-way bf16 split of the scales
+# would use.
 MFMA_BLOCK_PRODUCT_KINDS = 6
 MIX_MODES = ("2 FP8 MFMA + 1 FP32 outer-product MFMA + 32 FMA", "32 FMA only",
              "2 FP8 MFMA + 1 FP32 outer-product MFMA only")

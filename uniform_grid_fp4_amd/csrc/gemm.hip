@@ -16,8 +16,10 @@
 // broadcast to both 32-column blocks): an exact product rounded once, the
 // same value as an FP32 multiply, in the same lane/register layout as P.
 // What remains on the vector ALU is one FMA per output per block,
-// acc += S * P.  Vector instructions (4 issue cycles each) and the waits on
-// MFMA results bound this kernel, not the matrix core.  Nibbles are expanded
+// acc += S * P.  Per 32x32 tile and block the matrix core thus spends 32 + 32
+// cycles; on gfx950 the vector work of the other waves on a SIMD overlaps
+// that only a little, so the two add up, and staging, LDS fragment reads,
+// the barrier and waits on MFMA results come on top.  Nibbles are expanded
 // to FP8 (v_perm_b32 look-up) once per workgroup while staging into LDS, so
 // the waves read ready MFMA operands.
 //
@@ -34,6 +36,11 @@
 // range check returns zero past the tile's rows, so ragged edges need no
 // branches; full stages carry the stage offset in the scalar offset, and
 // only the last, partial stage tests each lane's block against the K range.
+// The four blocks of a stage are unrolled (LDS offsets become immediates);
+// an empty asm ties each block's fragments to the previous block's
+// accumulators, so the compiler issues a block's MFMAs only after the
+// previous block's FMAs instead of hoisting every block's MFMAs and holding
+// all their products in registers.
 // Tiles are assigned XCD-major: the 8 XCDs each walk a contiguous range of
 // tiles, so a row panel of A stays in one L2.
 #include <hip/hip_runtime.h>

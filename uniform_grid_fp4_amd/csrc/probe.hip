@@ -11,6 +11,7 @@
 //   kind 4  v_mfma_scale_f32_32x32x64_f8f6f4 fp4 E2M1
 //   kind 5  v_mfma_f32_32x32x16_bf16              (context)
 //   kind 6  v_mfma_f32_32x32x1_2b_f32             (the GEMM's scale products)
+//   kind 7  v_mfma_f32_32x32x8_bf16               (what a split-bf16 scale product would use)
 // Operands are arbitrary register contents (results are discarded); no
 // memory is touched except one guarded store per workgroup.
 //
@@ -27,6 +28,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 template <int KIND>
@@ -39,12 +41,15 @@ __global__ __launch_bounds__(256) void mfma_loop(float *out, int reps) {
   const long a = 0x3C3C3C3C3C3C3C3Cll + t, b = 0x3838383838383838ll - t;
   i32x8 a8, b8;
   bf16x8 ab;
+  s16x4 h4;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     a8[i] = 0x22222222 + t + i;
     b8[i] = 0x11111111 - t + i;
     ab[i] = (__bf16)(1.0f + 0.001f * (float)(t + i));
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h4[i] = (short)(0x3F80 + t + i);
   for (int r = 0; r < reps; ++r) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -60,6 +65,7 @@ __global__ __launch_bounds__(256) void mfma_loop(float *out, int reps) {
         acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[j], 4, 4, 0, 127, 0,
                                                                  127);
       if (KIND == 5) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ab, acc[j], 0, 0, 0);
+      if (KIND == 7) acc[j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(h4, h4, acc[j], 0, 0, 0);
       if (KIND == 6) {
         const f32x32 o = __builtin_amdgcn_mfma_f32_32x32x1f32(fa, fb, wide[j], 1, 0, 0);
         wide[j] = o;
@@ -165,6 +171,7 @@ double ufp4_probe_mfma_flops(int kind) {
     case 0: case 1: case 5: return 2.0 * 32 * 32 * 16;
     case 2: case 3: case 4: return 2.0 * 32 * 32 * 64;
     case 6: return 2.0 * 32 * 32 * 1 * 2;
+    case 7: return 2.0 * 32 * 32 * 8;
   }
   return 0.0;
 }
@@ -174,7 +181,7 @@ double ufp4_probe_mfma_flops(int kind) {
 // TFLOP/s (TOP/s for int8), or a negative value on a bad argument or a HIP
 // error.  Synchronises the device.
 double ufp4_probe_mfma_tflops(int kind, int wgs, int reps) {
-  if (kind < 0 || kind > 6 || wgs < 1 || wgs > (1 << 20) || reps < 1) return -1.0;
+  if (kind < 0 || kind > 7 || wgs < 1 || wgs > (1 << 20) || reps < 1) return -1.0;
   const double ms = time_ms(
       [&](float *out) {
         switch (kind) {
@@ -184,7 +191,8 @@ double ufp4_probe_mfma_tflops(int kind, int wgs, int reps) {
           case 3: return launch<3>(out, wgs, reps);
           case 4: return launch<4>(out, wgs, reps);
           case 5: return launch<5>(out, wgs, reps);
-          default: return launch<6>(out, wgs, reps);
+          case 6: return launch<6>(out, wgs, reps);
+          default: return launch<7>(out, wgs, reps);
         }
       },
       wgs);
