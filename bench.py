@@ -232,7 +232,18 @@ def cpu_baseline(L, target_s: float):
     g_rate = flops / tg
     elems_step = 2 * (T * H + F * H + T * F)
     step_s = elems_step / q_rate + 3 * 2.0 * T * H * F / g_rate
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] + [1])
+    blas = ", ".join(f"{i.get('internal_api', '?')} x{i.get('num_threads', '?')}" for i in pools)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": 3 * 2.0 * T * H * F / step_s / 1e12,
         "unit": "TFLOP/s",
@@ -241,7 +252,8 @@ def cpu_baseline(L, target_s: float):
         "sample": (f"oracle quantizer on {n_el} elements (64-row samples of X and dY, row- and "
                    f"column-wise, RTNE and SR: {q_rate / 1e6:.2f} M elem/s) and FP64 FPROP on "
                    f"{done} output rows ({g_rate / 1e9:.1f} GFLOP/s), scaled to one step "
-                   f"({step_s:.1f} s); host cpu_count={os.cpu_count()}"),
+                   f"({step_s:.1f} s); host {model}, cpu_count={os.cpu_count()}, "
+                   f"thread pools: {blas or 'none'}"),
     }
 
 
