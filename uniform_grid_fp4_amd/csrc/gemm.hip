@@ -42,7 +42,8 @@
 // previous block's FMAs instead of hoisting every block's MFMAs and holding
 // all their products in registers.
 // Tiles are assigned XCD-major: the 8 XCDs each walk a contiguous range of
-// tiles, so a row panel of A stays in one L2.
+// tiles, so a row panel of A stays in one L2.  Outputs are written with
+// nontemporal (streaming) stores: nothing in the kernel reads them back.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,8 +74,10 @@ constexpr int kXcds = 8;
 struct Stage {
   uint8_t a[kBM * kRowBytes];
   uint8_t b[kBN * kRowBytes];
-  float sa[kSB * kBM];   // block-major: sa[blk][row]
-  float sb[kSB * kBN];
+  // block-major scales sa[blk][row]; the 16-entry pad per block puts the four
+  // blocks of a row, which a quarter-wave stores together, in different banks
+  float sa[kSB * (kBM + 16)];
+  float sb[kSB * (kBN + 16)];
 };
 
 // 8 nibbles -> 8 FP8 E4M3 bytes.  Output byte order [n0 n2 n4 n6 | n1 n3 n5
@@ -146,6 +149,10 @@ struct Gemm {
       sq = 0;
       ss = 0;
     }
+    // the stage offsets are wave-uniform: keep them in scalar registers (the
+    // buffer loads' scalar offset), or the compiler loops over lanes
+    sq = __builtin_amdgcn_readfirstlane(sq);
+    ss = __builtin_amdgcn_readfirstlane(ss);
     const auto a = __builtin_amdgcn_raw_buffer_load_b64(ra_q, vq, sq, 0);
     r.aq[0] = make_uint2(a[0], a[1]);
     r.as[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra_s, vs, ss, 0));
@@ -159,11 +166,11 @@ struct Gemm {
     uint2 *da = reinterpret_cast<uint2 *>(s.a + row * kRowBytes + blk * 16);
     da[0] = nib8_to_fp8<GRID>(r.aq[0].x);
     da[1] = nib8_to_fp8<GRID>(r.aq[0].y);
-    s.sa[blk * kBM + row] = r.as[0];
+    s.sa[blk * (kBM + 16) + row] = r.as[0];
     uint2 *db = reinterpret_cast<uint2 *>(s.b + row * kRowBytes + blk * 16);
     db[0] = nib8_to_fp8<GRID>(r.bq[0].x);
     db[1] = nib8_to_fp8<GRID>(r.bq[0].y);
-    s.sb[blk * kBN + row] = r.bs[0];
+    s.sb[blk * (kBN + 16) + row] = r.bs[0];
   }
 
   // One stage: per block, the two 32x32 block products P (FP8 MFMA) and the
@@ -190,8 +197,8 @@ struct Gemm {
       long af = *reinterpret_cast<const long *>(pa + b * 16);
       long bf0 = *reinterpret_cast<const long *>(pb + b * 16);
       long bf1 = *reinterpret_cast<const long *>(pb + 32 * kRowBytes + b * 16);
-      float a1 = psa[b * kBM];
-      float b1 = psb[b * kBN];
+      float a1 = psa[b * (kBM + 16)];
+      float b1 = psb[b * (kBN + 16)];
       // this block's MFMAs may not start before the previous block's FMAs
       // are done (keeps the unrolled blocks from holding several blocks'
       // products in registers); the LDS reads above may run ahead
@@ -265,7 +272,8 @@ struct Gemm {
           const int dm = 8 * (r >> 2) + (r & 3);
           if (nt * 32 < nrem && dm < mrem) {
             const uint32_t u = __float_as_uint(acc[nt][r] * inv_g2);
-            cl[dm * ldc + nt * 32] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            __builtin_nontemporal_store((uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16),
+                                        cl + dm * ldc + nt * 32);
           }
         }
       }
@@ -276,12 +284,20 @@ struct Gemm {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int dm = 8 * (r >> 2) + (r & 3);
-          if (nt * 32 < nrem && dm < mrem) cl[dm * ldc + nt * 32] = acc[nt][r] * inv_g2;
+          if (nt * 32 < nrem && dm < mrem)
+            __builtin_nontemporal_store(acc[nt][r] * inv_g2, cl + dm * ldc + nt * 32);
         }
       }
     }
   }
 };
+
+// A wave-uniform 64-bit value held in scalar registers.
+__device__ __forceinline__ int64_t wave_uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ int64_t clampv(int64_t v, int64_t n) {
   return v < 0 ? 0 : (v > n ? n : v);
@@ -437,6 +453,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       job.kb0 = min(s_pre[e] / 16, kblocks);
       job.kb1 = min(s_pre[e + 1] / 16, kblocks);
       job.c_off = e * g.M * g.ldc + job.a_row0 * g.ldc + job.b_row0;
+    }
+    if (MODE != 0) {
+      // the group tables come from LDS: keep the tile's (uniform) bounds in
+      // scalar registers rather than in vector registers across the K loop
+      job.a_row0 = wave_uniform(job.a_row0);
+      job.a_rows = wave_uniform(job.a_rows);
+      job.b_row0 = wave_uniform(job.b_row0);
+      job.b_rows = wave_uniform(job.b_rows);
+      job.kb0 = wave_uniform(job.kb0);
+      job.kb1 = wave_uniform(job.kb1);
+      job.c_off = wave_uniform(job.c_off);
     }
     Gemm<GRID> gm(g, job);
     gm.run(stages);
