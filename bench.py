@@ -50,8 +50,8 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # of a plain 1 GiB device copy.  The figures hold for the GEMM source whose
 # SHA-256 is recorded with them; any other source reports null.
 GEMM_TRAFFIC = {
-    "dense-1.5B-fc1": {"sha256": "5bf9b9e659db18413c763ca5ad6c20ccd5379845ccbc4c8cd1ea4b67255df148",
-                       "bytes_per_launch": 390316948},
+    "dense-1.5B-fc1": {"sha256": "9a842f671bdd877ee7c8bf038175de5c995c84693eae44f0a475b8aeb6313873",
+                       "bytes_per_launch": 361991924},
 }
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
@@ -463,6 +463,8 @@ MFMA_KINDS = ("v_mfma_f32_32x32x16_fp8_fp8", "v_mfma_i32_32x32x16_i8",
 MFMA_BLOCK_PRODUCT_KINDS = 6
 MIX_MODES = ("2 FP8 MFMA + 1 FP32 outer-product MFMA + 32 FMA", "32 FMA only",
              "2 FP8 MFMA + 1 FP32 outer-product MFMA only")
+OVERLAP_KINDS = ("2 x v_mfma_f32_32x32x16_fp8_fp8", "1 x v_mfma_f32_32x32x1_2b_f32",
+                 "2 x v_mfma_f32_32x32x8_bf16")
 
 
 def probe_lib():
@@ -477,6 +479,8 @@ def probe_lib():
     L.ufp4_probe_mfma_flops.restype = ctypes.c_double
     L.ufp4_probe_mix_ms.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.ufp4_probe_mix_ms.restype = ctypes.c_double
+    L.ufp4_probe_overlap_ms.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.ufp4_probe_overlap_ms.restype = ctypes.c_double
     return L
 
 
@@ -534,6 +538,25 @@ def mfma_peaks(args):
                           "simd_cycles_per_wave_iteration": round(cyc[-1], 1)}), flush=True)
     print(json.dumps({"workload": "mfma-vs-valu", "mix_over_max_of_parts": round(cyc[0] / max(cyc[1:]), 3),
                       "mix_over_sum_of_parts": round(cyc[0] / (cyc[1] + cyc[2]), 3)}), flush=True)
+    # Cross-wave overlap: on every SIMD half of the waves issue one kind of
+    # matrix-core work (about 64 matrix-core cycles per iteration), the other
+    # half 32 FMAs per iteration; timed with each half alone and both
+    # together.  overlap = (alone + alone - together) / the shorter alone:
+    # 1 when the vector work hides entirely under the matrix-core work (or the
+    # reverse), 0 when the two serialise.
+    wgs, reps = 1024, 4000
+    for kind, name in enumerate(OVERLAP_KINDS):
+        t = []
+        for roles in (1, 2, 3):
+            ms = L.ufp4_probe_overlap_ms(kind, roles, wgs, reps)
+            if ms <= 0:
+                raise RuntimeError(f"overlap probe failed ({ms})")
+            t.append(ms)
+        print(json.dumps({"workload": "mfma-vs-valu-waves", "mfma": name,
+                          "mfma_waves_ms": round(t[0], 3), "fma_waves_ms": round(t[1], 3),
+                          "together_ms": round(t[2], 3),
+                          "overlap": round((t[0] + t[1] - t[2]) / min(t[0], t[1]), 3)}),
+              flush=True)
 
 
 def copy_ceiling(args):

@@ -228,6 +228,10 @@ def test_probe_library_loads_and_rejects_bad_arguments():
     assert L.ufp4_probe_mfma_tflops(0, 0, 1) == -1.0
     assert L.ufp4_probe_mix_ms(3, 1, 1) == -1.0
     assert L.ufp4_probe_mix_ms(0, 1, 0) == -1.0
+    assert L.ufp4_probe_overlap_ms(3, 1, 1, 1) == -1.0   # unknown matrix-core kind
+    assert L.ufp4_probe_overlap_ms(0, 0, 1, 1) == -1.0   # no role
+    assert L.ufp4_probe_overlap_ms(0, 4, 1, 1) == -1.0
+    assert L.ufp4_probe_overlap_ms(0, 3, 0, 1) == -1.0
 
 
 def test_size_limits_of_32_bit_offsets():

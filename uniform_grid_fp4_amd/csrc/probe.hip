@@ -19,6 +19,10 @@
 // FP8 MFMAs, one FP32 outer-product MFMA, 32 independent v_fmac_f32) and its
 // parts on their own, to show how far matrix-core and vector work overlap on
 // one SIMD.
+//
+// A third loop puts the matrix-core and the vector work in different waves
+// of one SIMD, to show which MFMA kinds the other waves' vector instructions
+// can overlap.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -122,6 +126,64 @@ __global__ __launch_bounds__(256) void mix_loop(float *out, int reps) {
   if (s == 1234.5f) out[blockIdx.x] = s;
 }
 
+// Cross-wave overlap: 512-thread workgroups, so SIMD s holds waves s and s+4
+// of each workgroup.  Waves 0-3 issue matrix-core work (ROLES bit 0), waves
+// 4-7 issue 32 independent v_fmac_f32 per iteration (bit 1); with one bit
+// set the other half of the waves exits at once.  KIND 0: two FP8 MFMAs
+// (v_mfma_f32_32x32x16_fp8_fp8), 1: one FP32 outer-product MFMA
+// (v_mfma_f32_32x32x1_2b_f32), 2: two v_mfma_f32_32x32x8_bf16 -- each about
+// 64 matrix-core cycles per iteration.
+template <int KIND, int ROLES>
+__global__ __launch_bounds__(512) void overlap_loop(float *out, int reps) {
+  const int t = threadIdx.x;
+  const int w = t >> 6;
+  const long a = 0x3C3C3C3C3C3C3C3Cll + t, b = 0x3838383838383838ll - t;
+  const float fa = 1.0f + 0.001f * (float)t, fb = 1.0f - 0.001f * (float)t;
+  const float m = 1.0001f + 1e-9f * (float)t, c = 0.5f;
+  s16x4 h4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h4[i] = (short)(0x3F80 + t + i);
+  f32x16 p0 = {}, p1 = {};
+  f32x32 sc = {};
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = (float)(t + i);
+  if (w < 4 && (ROLES & 1)) {
+    for (int r = 0; r < reps; ++r) {
+      if (KIND == 0) {
+        p0 = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, p1, 0, 0, 0);
+      } else if (KIND == 1) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x1f32(fa, fb, sc, 1, 0, 0);
+      } else {
+        p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(h4, h4, p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(h4, h4, p1, 0, 0, 0);
+      }
+    }
+  }
+  if (w >= 4 && (ROLES & 2)) {
+    for (int r = 0; r < reps; ++r) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        asm volatile(UFP4_FMAC16
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                       "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                       "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+                     : "v"(m), "v"(c));
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += v[i] + p0[i] + p1[i] + sc[i] + sc[16 + i];
+  if (s == 1234.5f) out[blockIdx.x] = s;
+}
+
+template <int KIND, int ROLES>
+hipError_t launch_overlap(float *out, int wgs, int reps) {
+  hipLaunchKernelGGL((overlap_loop<KIND, ROLES>), dim3(wgs), dim3(512), 0, 0, out, reps);
+  return hipGetLastError();
+}
+
 template <int KIND>
 hipError_t launch(float *out, int wgs, int reps) {
   hipLaunchKernelGGL(mfma_loop<KIND>, dim3(wgs), dim3(256), 0, 0, out, reps);
@@ -214,6 +276,30 @@ double ufp4_probe_mix_ms(int mode, int wgs, int reps) {
           case 1: return launch_mix<1>(out, wgs, reps);
           default: return launch_mix<2>(out, wgs, reps);
         }
+      },
+      wgs);
+}
+
+// Runs the cross-wave overlap loop (kind 0 FP8, 1 FP32 outer product, 2 bf16
+// K = 8; roles 1 = matrix-core waves only, 2 = FMA waves only, 3 = both) on
+// `wgs` workgroups of 8 waves and returns the elapsed milliseconds, or a
+// negative value on a bad argument or a HIP error.  Synchronises the device.
+double ufp4_probe_overlap_ms(int kind, int roles, int wgs, int reps) {
+  if (kind < 0 || kind > 2 || roles < 1 || roles > 3 || wgs < 1 || wgs > (1 << 20) || reps < 1)
+    return -1.0;
+  return time_ms(
+      [&](float *out) {
+#define UFP4_OV(K)                                              \
+  if (kind == K) {                                              \
+    if (roles == 1) return launch_overlap<K, 1>(out, wgs, reps); \
+    if (roles == 2) return launch_overlap<K, 2>(out, wgs, reps); \
+    return launch_overlap<K, 3>(out, wgs, reps);                 \
+  }
+        UFP4_OV(0)
+        UFP4_OV(1)
+        UFP4_OV(2)
+#undef UFP4_OV
+        return hipErrorInvalidValue;
       },
       wgs);
 }
