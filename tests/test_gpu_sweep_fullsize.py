@@ -1,0 +1,80 @@
+"""GPU parity of the quantizer at the sweep workload's full size: a 16384 x
+16384 bf16 tensor (2^28 elements) drawn from a Gaussian, a Laplace and a
+Student-t (nu = 3) distribution, quantized row-wise and column-wise
+(transposed output), onto the uniform and the E2M1 grid, with RTNE and with
+stochastic rounding, with and without the RHT -- the calls and arguments
+`bench.py --workload quant-sweep` times.  The oracle recomputes sampled
+output rows one by one (the first, the last and random ones; for the
+column-wise output a row is a whole input column), and codes and scales must
+match bit for bit, SR included (the sampled rows draw the SR bits of their
+position in the full output).  One dual-axis call per tensor is checked the
+same way.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ufp4_oracle as O
+from uniform_grid_fp4_amd import ufp4 as U
+from uniform_grid_fp4_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MASK, SEED, SID = 0xBEEF, 7, 0      # the sweep's sign mask, SR seed and stream
+
+
+def sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=k)])).astype(np.int64)
+
+
+def check_sampled(q, x, axis, rht, grid, rnd, rows, sid=SID, mask=MASK, what=""):
+    """Output rows `rows` of q equal the oracle's quantization of the same
+    input rows (row-wise) or input columns (column-wise)."""
+    r = torch.as_tensor(rows, device=x.device)
+    if axis == U.BLOCKS_ALONG_COLS:
+        xb = O.to_blocked_rows(O.bf16_bits_to_f32(W.bits_numpy(x[r])), O.AXIS_COLS)
+    else:
+        xb = O.to_blocked_rows(O.bf16_bits_to_f32(W.bits_numpy(x[:, r])), O.AXIS_ROWS)
+    assert xb.shape[1] == q.kpad
+    nib, s = O.quantize_blocked(xb, rht, mask, grid, rnd, SEED, sid, row_ids=rows)
+    gc = q.codes[r].cpu().numpy()
+    gs = q.scales[r].cpu().numpy()
+    assert np.array_equal(gc, O.pack_nibbles(nib)), f"{what}: codes differ"
+    assert np.array_equal(gs.view(np.uint32), s.view(np.uint32)), f"{what}: scales differ"
+
+
+@pytest.fixture(scope="module", params=W.SWEEP_DISTS)
+def sweep(request):
+    x = W.sweep_tensor(request.param, DEV)
+    assert tuple(x.shape) == W.SWEEP_SHAPE == (16384, 16384)
+    yield request.param, x
+    del x
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("axis", [U.BLOCKS_ALONG_COLS, U.BLOCKS_ALONG_ROWS])
+def test_sweep_quantizer_full_size(sweep, axis):
+    dist, x = sweep
+    n = x.shape[0]
+    for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
+        for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+            for rht in (False, True):
+                q = U.ufp4_rht_quantize(x, axis, rht, MASK, grid, rnd, SEED, SID)
+                rows = sample(n, 6, 100 * grid + 10 * rnd + int(rht) + 7 * axis)
+                what = f"{dist} axis={axis} grid={grid} rnd={rnd} rht={rht}"
+                check_sampled(q, x, axis, rht, grid, rnd, rows, what=what)
+                del q
+
+
+def test_sweep_dual_quantizer_full_size(sweep):
+    """The dual-axis kernel on the full sweep tensor (UFP4: uniform grid, RHT,
+    SR; the two outputs on SR streams 0 and 1, different sign masks)."""
+    dist, x = sweep
+    q_r, q_c = U.ufp4_rht_quantize_dual(x, (True, MASK, 0), (True, 0x1234, 1),
+                                        grid=U.GRID_UNIFORM, rnd=U.ROUND_SR, seed=SEED)
+    rows = sample(x.shape[0], 6, 5)
+    check_sampled(q_r, x, U.BLOCKS_ALONG_COLS, True, U.GRID_UNIFORM, U.ROUND_SR, rows, sid=0,
+                  mask=MASK, what=f"{dist} dual row-wise")
+    check_sampled(q_c, x, U.BLOCKS_ALONG_ROWS, True, U.GRID_UNIFORM, U.ROUND_SR, rows, sid=1,
+                  mask=0x1234, what=f"{dist} dual column-wise")
