@@ -139,12 +139,14 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // Column-wise: blocks along the strided dimension, output transposed.
-// A workgroup (4 waves) owns a tile of 256 padded rows (16 blocks) x 128
-// columns.  Wave w quantizes row-blocks w, w+4, w+8, w+12; in each, lane l
-// loads one dword (columns 2l, 2l+1) of the 16 rows, so every row is read as
-// 256 contiguous bytes, and the block's rows come from one wave-uniform buffer
-// resource.  The quantized blocks go to LDS and the tile is written back as
-// 128 output rows of 128 contiguous bytes of codes and 64 bytes of scales.
+// A workgroup (4 waves) owns a tile of 256 padded rows (16 blocks) x 64*CW
+// columns, CW = 2 or 4 columns per lane (4 for large aligned inputs: each row
+// is then read as 512 contiguous bytes per wave, which HBM serves better than
+// 256).  Wave w quantizes row-blocks w, w+4, w+8, w+12; in each, lane l loads
+// columns CW*l .. CW*l+CW-1 of the 16 rows, and the block's rows come from one
+// wave-uniform buffer resource.  The quantized blocks go to LDS and the tile
+// is written back as 64*CW output rows of 128 contiguous bytes of codes and 64
+// bytes of scales.
 // Groups: padded block p belongs to the group e with P_e <= 16p < P_{e+1};
 // its rows are off_e + (16p - P_e) + j, zero past the group's end.
 // ---------------------------------------------------------------------------
@@ -244,21 +246,85 @@ __device__ __forceinline__ void load_col_block(const uint16_t *__restrict__ x, i
   }
 }
 
+// Raw dwords of one block of 16 rows for this lane's CW (2 or 4) columns:
+// w[j][c] holds columns 2c, 2c+1 of row j.  With VEC the lane reads CW
+// columns with one 4- or 8-byte load per row (rows then need CW-element
+// alignment and n_cols a multiple of CW, so a load is wholly in or out of the
+// resource); otherwise 2-byte loads.  Out-of-resource reads return zero.
+template <bool VEC, int CW>
+__device__ __forceinline__ void load_col_rows(const uint16_t *__restrict__ x, int64_t ld,
+                                              int64_t n_cols, int64_t row0, int valid,
+                                              int colb, const uint32_t (&keep)[CW / 2],
+                                              uint32_t (&w)[16][CW / 2]) {
+  const int64_t nbytes = valid > 0 ? ((int64_t)(valid - 1) * ld + n_cols) * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x + row0 * ld), (short)0, (int)nbytes, 0x00020000);
+  const int ld2 = (int)(ld * 2);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int off = j * ld2 + colb;
+    if (VEC && CW == 2) {
+      w[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0) & keep[0];
+    } else if (VEC) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+#pragma unroll
+      for (int c = 0; c < CW / 2; ++c) w[j][c] = v[c] & keep[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < CW / 2; ++c) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4 * c, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4 * c + 2, 0, 0);
+        w[j][c] = (lo | (hi << 16)) & keep[c];
+      }
+    }
+  }
+}
+
+// Column-wise tile order.  The tiles of one input (row-band pt, column tile
+// ct) are numbered with ORD row bands interleaved (ORD = 1: down a column
+// strip first), and the workgroups of each XCD (workgroups are dealt to the 8
+// XCDs round robin) take a contiguous range of that numbering, so the tiles an
+// XCD runs together write neighbouring pieces of the same output rows and
+// those merge in its L2 before they reach HBM.
+__device__ __forceinline__ void col_tile_coords(int64_t tile, int64_t n_ptiles, int64_t n_ctiles,
+                                                int ord, int64_t &pt, int64_t &ct) {
+  const int64_t gsz = (int64_t)ord * n_ctiles;
+  const int64_t grp = tile / gsz, r = tile - grp * gsz;
+  const int64_t left = n_ptiles - grp * ord;
+  const int64_t gb = left < ord ? left : ord;
+  pt = grp * ord + r % gb;
+  ct = r / gb;
+}
+
+// A permutation of the workgroup ids when the grid is a multiple of 8 (the
+// launchers make it one), else the identity.
+__device__ __forceinline__ int64_t xcd_major_block() {
+  if (gridDim.x % 8 != 0) return blockIdx.x;
+  return (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+}
+
 // Stacked mode (n_stack > 1, not GROUPED): the input rows are n_stack equal
 // groups of n_rows rows, each quantized on its own and written as output rows
 // [s * n_cols, (s + 1) * n_cols).
-template <int GRID, int RND, bool RHT, bool VEC, bool GROUPED>
+template <int GRID, int RND, bool RHT, bool VEC, bool GROUPED, int CW>
 __global__ __launch_bounds__(256) void quant_cols_kernel(
     const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
     const int64_t *__restrict__ goff, int n_groups, int64_t n_stack, int64_t kpad,
     uint8_t *__restrict__ codes, float *__restrict__ scales, uint32_t sign_mask,
     uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id) {
+  constexpr int kCols = 64 * CW;                 // tile columns
+  constexpr int kTB = kColTileRows / 16;         // tile row-blocks
+  // Narrow tiles prefetch the next row-block and walk down column strips;
+  // wide ones hold twice the columns per lane, so they load one row-block at
+  // a time (occupancy hides the latency) and interleave 4 row bands.
+  constexpr bool kPrefetch = CW == 2;
+  constexpr int kOrd = CW == 2 ? 1 : 4;
   constexpr int kTabs = GROUPED ? kMaxGroups + 1 : 1;
   __shared__ int64_t s_off[kTabs];
   __shared__ int64_t s_poff[kTabs];
   __shared__ int64_t s_scan[GROUPED ? 256 : 1];
-  __shared__ uint2 s_codes[kColTileCols][kColTileRows / 16 + 1];
-  __shared__ float s_scales[kColTileCols][kColTileRows / 16 + 1];
+  __shared__ uint2 s_codes[kCols][kTB + 1];
+  __shared__ float s_scales[kCols][kTB + 1];
 
   int64_t padded_end;
   if (GROUPED) {
@@ -273,7 +339,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t kblocks = kpad / 16;
   const int64_t n_ptiles = (kpad + kColTileRows - 1) / kColTileRows;
-  const int64_t n_ctiles = (n_cols + kColTileCols - 1) / kColTileCols;
+  const int64_t n_ctiles = (n_cols + kCols - 1) / kCols;
   const int64_t per_stack = n_ptiles * n_ctiles;
   const int64_t total = per_stack * n_stack;
 
@@ -297,72 +363,85 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
     valid = __builtin_amdgcn_readfirstlane(valid);
   };
 
-  // Column tiles vary fastest, so the workgroups in flight together cover
-  // whole input rows (contiguous DRAM pages) rather than a narrow strip of
-  // many rows.
-  for (int64_t tile_all = blockIdx.x; tile_all < total; tile_all += gridDim.x) {
+  for (int64_t tile_all = xcd_major_block(); tile_all < total; tile_all += gridDim.x) {
     const int64_t si = tile_all / per_stack;
-    const int64_t tile = tile_all - si * per_stack;
-    const int64_t pt = tile / n_ctiles;
-    const int64_t ct = tile - pt * n_ctiles;
+    int64_t pt, ct;
+    col_tile_coords(tile_all - si * per_stack, n_ptiles, n_ctiles, kOrd, pt, ct);
     const uint16_t *xs = x + si * n_rows * ld;
     const int64_t out_row0 = si * n_cols;          // first output row of this stack
-    const int64_t pb0 = pt * (kColTileRows / 16);   // first padded block of the tile
-    const int64_t col0 = ct * kColTileCols;
-    const int64_t col = col0 + 2 * lane;
-    const uint32_t keep = (col + 1 < n_cols) ? 0xFFFFFFFFu : (col < n_cols ? 0x0000FFFFu : 0u);
-    const int col2 = (int)(col * 2);
-    // Wave w quantizes row-blocks w, w+4, w+8, w+12 of the tile; the loads of
-    // the next row-block are in flight while the current one is quantized.
-    uint32_t cur[16], nxt[16];
+    const int64_t pb0 = pt * kTB;                   // first padded block of the tile
+    const int64_t col0 = ct * kCols;
+    const int64_t col = col0 + CW * lane;
+    uint32_t keep[CW / 2];
+#pragma unroll
+    for (int c = 0; c < CW / 2; ++c) {
+      const int64_t cc = col + 2 * c;
+      keep[c] = (cc + 1 < n_cols) ? 0xFFFFFFFFu : (cc < n_cols ? 0x0000FFFFu : 0u);
+    }
+    const int colb = (int)(col * 2);
+    // Wave w quantizes row-blocks w, w+4, w+8, w+12 of the tile.
+    uint32_t cur[16][CW / 2], nxt[16][CW / 2];
     int64_t row0;
     int valid;
     block_rows(pb0 + wave, row0, valid);
-    load_col_block<VEC>(xs, ld, n_cols, row0, valid, col2, keep, cur);
+    load_col_rows<VEC, CW>(xs, ld, n_cols, row0, valid, colb, keep, cur);
 #pragma unroll 1
     for (int q = 0; q < 4; ++q) {
       const int rb = wave + 4 * q;                    // block within the tile (wave-uniform)
       const int64_t p = pb0 + rb;                     // padded block index
-      if (q < 3) {
+      if (kPrefetch && q < 3) {
         block_rows(p + 4, row0, valid);
-        load_col_block<VEC>(xs, ld, n_cols, row0, valid, col2, keep, nxt);
+        load_col_rows<VEC, CW>(xs, ld, n_cols, row0, valid, colb, keep, nxt);
       }
-      float va[16], vb[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        va[j] = bf16_lo(cur[j], RHT ? sign_bit(sign_mask, j) : 0u);
-        vb[j] = bf16_hi(cur[j], RHT ? sign_bit(sign_mask, j) : 0u);
+      for (int c = 0; c < CW / 2; ++c) {
+        float va[16], vb[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          va[j] = bf16_lo(cur[j][c], RHT ? sign_bit(sign_mask, j) : 0u);
+          vb[j] = bf16_hi(cur[j][c], RHT ? sign_bit(sign_mask, j) : 0u);
+        }
+        uint32_t a0, a1, b0, b1;
+        float sa, sb;
+        const uint64_t base_a =
+            (uint64_t)(out_row0 + col + 2 * c) * (uint64_t)kpad + (uint64_t)p * 16u;
+        const uint64_t base_b = base_a + (uint64_t)kpad;
+        quantize_block<GRID, RND, RHT>(va, base_a, seed_lo, seed_hi, stream_id, a0, a1, sa);
+        quantize_block<GRID, RND, RHT>(vb, base_b, seed_lo, seed_hi, stream_id, b0, b1, sb);
+        s_codes[CW * lane + 2 * c][rb] = make_uint2(a0, a1);
+        s_codes[CW * lane + 2 * c + 1][rb] = make_uint2(b0, b1);
+        s_scales[CW * lane + 2 * c][rb] = sa;
+        s_scales[CW * lane + 2 * c + 1][rb] = sb;
       }
-      uint32_t a0, a1, b0, b1;
-      float sa, sb;
-      const uint64_t base_a = (uint64_t)(out_row0 + col) * (uint64_t)kpad + (uint64_t)p * 16u;
-      const uint64_t base_b = base_a + (uint64_t)kpad;
-      quantize_block<GRID, RND, RHT>(va, base_a, seed_lo, seed_hi, stream_id, a0, a1, sa);
-      quantize_block<GRID, RND, RHT>(vb, base_b, seed_lo, seed_hi, stream_id, b0, b1, sb);
-      s_codes[2 * lane][rb] = make_uint2(a0, a1);
-      s_codes[2 * lane + 1][rb] = make_uint2(b0, b1);
-      s_scales[2 * lane][rb] = sa;
-      s_scales[2 * lane + 1][rb] = sb;
       if (q < 3) {
+        if (kPrefetch) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+          for (int j = 0; j < 16; ++j)
+#pragma unroll
+            for (int c = 0; c < CW / 2; ++c) cur[j][c] = nxt[j][c];
+        } else {
+          block_rows(p + 4, row0, valid);
+          load_col_rows<VEC, CW>(xs, ld, n_cols, row0, valid, colb, keep, cur);
+        }
       }
     }
     __syncthreads();
-    // write back: 128 columns x 16 blocks of 8-byte codes; 16 consecutive
+    // write back: kCols columns x 16 blocks of 8-byte codes; 16 consecutive
     // lanes write one column's 128 contiguous bytes
-    const int nb = (int)((kblocks - pb0) < 16 ? (kblocks - pb0) : 16);
+    const int nb = (int)((kblocks - pb0) < kTB ? (kblocks - pb0) : kTB);
     const int blk = tid & 15;
     const int c0 = tid >> 4;                           // 0..15, then +16 per step
     uint8_t *dq = codes + (out_row0 + col0 + c0) * (kpad / 2) + (pb0 + blk) * 8;
     float *ds = scales + (out_row0 + col0 + c0) * kblocks + pb0 + blk;
     const int64_t step_q = 16 * (kpad / 2), step_s = 16 * kblocks;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < kCols / 16; ++it) {
       const int c = c0 + 16 * it;
       if (col0 + c < n_cols && blk < nb) {
-        *reinterpret_cast<uint2 *>(dq) = s_codes[c][blk];
-        *ds = s_scales[c][blk];
+        // streaming stores: a later kernel reads the operand
+        const uint2 cv = s_codes[c][blk];
+        __builtin_nontemporal_store(((uint64_t)cv.y << 32) | cv.x, reinterpret_cast<uint64_t *>(dq));
+        __builtin_nontemporal_store(s_scales[c][blk], ds);
       }
       dq += step_q;
       ds += step_s;
@@ -685,20 +764,17 @@ static hipError_t launch_rows_t(const QuantArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int GRID, int RND, bool RHT>
-static hipError_t launch_cols_t(const QuantArgs &a, hipStream_t st) {
+template <int GRID, int RND, bool RHT, int CW>
+static hipError_t launch_cols_cw(const QuantArgs &a, bool vec, hipStream_t st) {
   const int64_t n_ptiles = (a.kpad + kColTileRows - 1) / kColTileRows;
-  const int64_t n_ctiles = (a.n_cols + kColTileCols - 1) / kColTileCols;
+  const int64_t n_ctiles = (a.n_cols + 64 * CW - 1) / (64 * CW);
   const int64_t n_stack = a.axis == 2 ? a.n_groups : 1;
   const int64_t rows_per = a.n_rows / n_stack;
-  const int blocks = grid_for(n_ptiles * n_ctiles * n_stack, 1, 256 * 8);
-  // dword loads need 4-byte aligned rows and an even column count (a dword
-  // straddling the last column of the last row would read as zero)
-  const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0) &&
-                   (a.n_cols % 2 == 0);
+  int blocks = grid_for(n_ptiles * n_ctiles * n_stack, 1, 256 * 16);
+  if (blocks >= 8) blocks -= blocks % 8;   // whole XCD rounds (xcd_major_block)
 #define UFP4_QC(V, G)                                                                          \
-  hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, V, G>), dim3(blocks), dim3(256), 0, st, \
-                     a.x, rows_per, a.n_cols, a.ld, a.goff, a.n_groups, n_stack, a.kpad,        \
+  hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, V, G, CW>), dim3(blocks), dim3(256), 0, \
+                     st, a.x, rows_per, a.n_cols, a.ld, a.goff, a.n_groups, n_stack, a.kpad,    \
                      a.codes, a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id)
   const bool grouped = a.goff != nullptr;
   if (vec) {
@@ -708,6 +784,25 @@ static hipError_t launch_cols_t(const QuantArgs &a, hipStream_t st) {
   }
 #undef UFP4_QC
   return hipGetLastError();
+}
+
+template <int GRID, int RND, bool RHT>
+static hipError_t launch_cols_t(const QuantArgs &a, hipStream_t st) {
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
+  // Four columns per lane need 8-byte loads: 8-byte aligned rows and a column
+  // count that is a multiple of 4 (so no load straddles the end of a row).
+  // They pay off once there are enough wide tiles to fill the GPU several
+  // times over; smaller inputs keep two columns per lane.
+  const bool vec4 = (xa & 7u) == 0 && a.ld % 4 == 0 && a.n_cols % 4 == 0;
+  const int64_t n_stack = a.axis == 2 ? a.n_groups : 1;
+  const int64_t wide_tiles =
+      ((a.kpad + kColTileRows - 1) / kColTileRows) * ((a.n_cols + 255) / 256) * n_stack;
+  if (vec4 && wide_tiles >= 8 * (int64_t)device_cus())
+    return launch_cols_cw<GRID, RND, RHT, 4>(a, true, st);
+  // dword loads need 4-byte aligned rows and an even column count (a dword
+  // straddling the last column of the last row would read as zero)
+  const bool vec = (xa & 3u) == 0 && a.ld % 2 == 0 && a.n_cols % 2 == 0;
+  return launch_cols_cw<GRID, RND, RHT, 2>(a, vec, st);
 }
 
 template <int GRID, int RND>
