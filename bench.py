@@ -354,7 +354,9 @@ def quant_sweep(args):
     tensor (512 MiB) does not fit the 256 MiB MALL, so every call streams from
     HBM.  Each case also reports the pages' quantization diagnostics from the
     library's diagnostics kernel (SQNR, 1 - alpha, delta_mag, underflow ratio,
-    bucket utilization) and, for the RHT case, the SQNR change RHT brings."""
+    bucket utilization) and, for the RHT case, the SQNR change RHT brings.
+    Per tensor, the dual-axis quantizer (uniform grid, RHT on both outputs,
+    RTNE and SR) is timed too, over its 3.5 algorithmic bytes per element."""
     import torch
     from uniform_grid_fp4_amd import ufp4 as U
     from uniform_grid_fp4_amd import workloads as W
@@ -394,6 +396,29 @@ def quant_sweep(args):
                             "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                             **diag}), flush=True)
                         del q
+        # the dual-axis quantizer (both operands of the tensor from one read),
+        # uniform grid with RHT on both outputs, as the UFP4 recipe uses it
+        for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+            sides = ((True, 0xBEEF, 0), (True, 0x1DEA, 1))
+            qr, qc = U.ufp4_rht_quantize_dual(x, *sides, grid=U.GRID_UNIFORM, rnd=rnd, seed=7)
+            for _ in range(args.warmup):
+                U.ufp4_rht_quantize_dual(x, *sides, grid=U.GRID_UNIFORM, rnd=rnd, seed=7,
+                                         out_rows=qr, out_cols=qc)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                U.ufp4_rht_quantize_dual(x, *sides, grid=U.GRID_UNIFORM, rnd=rnd, seed=7,
+                                         out_rows=qr, out_cols=qc)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            gbs = n * BYTES_PER_DUAL_ELEM / (ms * 1e-3) / 1e9
+            print(json.dumps({"workload": "quant-sweep", "dist": dist, "layout": "dual-axis",
+                              "rht": True, "grid": "uniform", "rounding": "sr" if rnd else "rtne",
+                              "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+            del qr, qc
         del x
         torch.cuda.empty_cache()
 
