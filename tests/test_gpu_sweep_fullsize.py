@@ -78,3 +78,29 @@ def test_sweep_dual_quantizer_full_size(sweep):
                   mask=MASK, what=f"{dist} dual row-wise")
     check_sampled(q_c, x, U.BLOCKS_ALONG_ROWS, True, U.GRID_UNIFORM, U.ROUND_SR, rows, sid=1,
                   mask=0x1234, what=f"{dist} dual column-wise")
+
+
+@pytest.mark.parametrize("ld_extra", [0, 8, 2])
+def test_column_wise_wide_tiles_ragged(ld_extra):
+    """Large column-wise inputs take the kernel's four-columns-per-lane tiles
+    (8-byte row loads) when rows are 8-byte aligned and the column count is a
+    multiple of 4; ld_extra = 2 breaks that alignment and takes the two-column
+    tiles at the same size.  Ragged rows (16380) and a ragged last column tile
+    (8200 = 32 * 256 + 8 columns), contiguous and strided rows; sampled output
+    rows (input columns, the last tile's all included) bit-exact against the
+    oracle for both grids, RTNE and SR."""
+    n_rows, n_cols = 16380, 8200
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11 + ld_extra)
+    base = torch.randn(n_rows, n_cols + ld_extra, device=DEV, generator=g).to(torch.bfloat16)
+    x = base[:, :n_cols]
+    assert x.stride(0) == n_cols + ld_extra
+    cols = np.unique(np.concatenate([sample(n_cols, 6, 3 + ld_extra),
+                                     np.arange(8188, n_cols)])).astype(np.int64)
+    for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
+        for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+            q = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_ROWS, True, MASK, grid, rnd, SEED, SID)
+            assert q.rows == n_cols and q.kpad == 16384
+            check_sampled(q, x, U.BLOCKS_ALONG_ROWS, True, grid, rnd, cols,
+                          what=f"wide ld+{ld_extra} grid={grid} rnd={rnd}")
+            del q
