@@ -13,8 +13,11 @@ region.
 
 Prints one JSON line.  `value` is the whole step's throughput in GEMM
 TFLOP/s (3 x 2*T*H*F FLOP per step over the wall time of the step, the
-quantizations included); the quantizer and GEMM kernels are also reported on
-their own, timed with HIP events on the stream they run on.
+quantizations included).  The step is captured once as a HIP graph and the
+timed steps are replays of it (checked bit-identical to the eager step
+first; `--eager` times eager launches instead); the quantizer and GEMM
+kernels are also reported on their own, timed with HIP events on the stream
+they run on in an eager pass.
 """
 from __future__ import annotations
 
@@ -79,6 +82,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as eager launches instead of replays of the step "
+                         "captured once as a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--quantizer", default="dual", choices=["single", "dual"],
@@ -169,6 +175,10 @@ class Step:
         dytq = self.quant("q_dyt_wgrad", L.dy, R, self.mw, U.ROUND_SR, 1, ev)
         xtq = self.quant("q_xt_wgrad", L.x, R, self.mw, U.ROUND_RTNE, 0, ev)
         self.gemm("wgrad", U.ufp4_gemm_wgrad, dytq, xtq, self.dw, ev)
+
+    def outputs(self):
+        """The step's GEMM outputs (they depend on every quantized operand)."""
+        return [self.y, self.dx, self.dw]
 
     QUANT = ("q_x_fprop", "q_w_fprop", "q_dy_dgrad", "q_wt_dgrad", "q_dyt_wgrad", "q_xt_wgrad")
     QUANT_DUAL = ("q_x_dual", "q_w_dual", "q_dy_dual")
@@ -318,6 +328,9 @@ class MoeStep(Step):
         xtq = self.quant("q_xt_wgrad", L.x, R, self.mw, U.ROUND_RTNE, 0, ev,
                          group_offsets=self.offd)
         self.gemm("wgrad", U.WGRAD, dytq, xtq, self.dwg, ev)
+
+    def outputs(self):
+        return [self.y, self.dx, self.dwg]
 
     def quant_elems(self):
         T, H, F, E = self.tokens, self.H, self.F, self.E
@@ -655,6 +668,37 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
+    ms_step_eager = ms_step
+    graph_checked = None
+    if not args.eager:
+        # The step captured once as a HIP graph (stream capture of the same
+        # library calls on the same buffers) and replayed: no per-launch host
+        # work or gaps.  Each of three checking replays first has its outputs
+        # overwritten with NaN and must reproduce the eager step bit for bit.
+        outs = st.outputs()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.run(None)
+        for _ in range(3):
+            st.run(None)
+            torch.cuda.synchronize()
+            ref = [t.clone() for t in outs]
+            for t in outs:
+                t.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert all(torch.equal(a, b) for a, b in zip(outs, ref)), \
+                "graph replay differs from the eager step"
+        graph_checked = 3
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
     dur = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}
     q_ms = sum(dur[n] for n in st.quant_names)
     q_bytes = sum(st.quant_bytes().values())
@@ -674,6 +718,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "timing": ("HIP graph replays of the captured step (%d checking replays bit-identical "
+                   "to the eager step); kernel durations from an eager pass with HIP events"
+                   % graph_checked) if graph_checked else "eager launches with HIP events",
+        "ms_per_step_eager": round(ms_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
