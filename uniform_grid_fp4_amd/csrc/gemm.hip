@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "ufp4_device.h"
 #include "ufp4_kernels.h"
 
@@ -481,12 +483,19 @@ static size_t smem_bytes(int mode) {
 template <int GRID, int MODE>
 static hipError_t launch_t(const GemmArgs &g, int64_t blocks, hipStream_t st) {
   const size_t sm = smem_bytes(MODE);
-  static bool configured = false;
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<GRID, MODE>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  // The dynamic-LDS limit is a per-device function attribute: set it once on
+  // each device the kernel runs on (a bit per device id; concurrent first
+  // calls at worst both set it, which is harmless).
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit == 0 || (configured.load(std::memory_order_acquire) & bit) == 0) {
+    e = hipFuncSetAttribute((const void *)gemm_kernel<GRID, MODE>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL((gemm_kernel<GRID, MODE>), dim3((unsigned)blocks), dim3(kThreads), sm, st, g);
   return hipGetLastError();
