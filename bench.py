@@ -701,7 +701,8 @@ def main():
 
     dur = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}
     q_ms = sum(dur[n] for n in st.quant_names)
-    q_bytes = sum(st.quant_bytes().values())
+    qb = st.quant_bytes()
+    q_bytes = sum(qb.values())
     g_ms = sum(dur[n] for n in Step.GEMMS)
     g_flop = 3 * st.gemm_flops()
     gemm_avg_ms = g_ms / 3
@@ -735,6 +736,8 @@ def main():
                      "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "ms_per_step": round(q_ms, 4),
                      "per_call_ms": {n: round(dur[n], 4) for n in st.quant_names},
+                     "per_call_gbs": {n: round(qb[n] / (dur[n] * 1e-3) / 1e9, 1)
+                                      for n in st.quant_names},
                      "kernels": "dual-axis" if st.dual else "single-axis",
                      "bytes_per_step": q_bytes},
         "gemm": {"tflops": round(gemm_tflops, 2),
