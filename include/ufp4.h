@@ -30,7 +30,11 @@
  *     library never allocates, frees or synchronises, and keeps no mutable
  *     global state).  Descriptor structs are HOST memory read during the call.
  *   - Work is enqueued on `stream` and runs asynchronously; results are valid
- *     once the stream has reached that point.
+ *     once the stream has reached that point.  A call enqueues kernel
+ *     launches only (no copy, memset or allocation), so a sequence of calls
+ *     can be stream-captured into a HIP graph and replayed.  The first GEMM
+ *     call of each kind on a device also sets a one-time kernel attribute;
+ *     make it before capturing.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     failed check returns a negative status and enqueues nothing.  A HIP
  *     launch failure returns UFP4_ERR_HIP.
