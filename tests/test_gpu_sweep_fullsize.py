@@ -104,3 +104,37 @@ def test_column_wise_wide_tiles_ragged(ld_extra):
             check_sampled(q, x, U.BLOCKS_ALONG_ROWS, True, grid, rnd, cols,
                           what=f"wide ld+{ld_extra} grid={grid} rnd={rnd}")
             del q
+
+
+def test_column_wise_wide_tiles_grouped():
+    """The four-column tiles in the grouped (per-expert padded) mode: 16000
+    rows in 50 groups of ragged sizes, some empty, 8200 columns.  Sampled
+    output rows bit-exact against the oracle (RTNE and SR), and the whole
+    output equal to the dual-axis kernel's column-wise output, which tiles
+    differently (two columns per lane, its own loads and tile order)."""
+    n_rows, n_cols, n_groups = 16000, 8200, 50
+    rng = np.random.default_rng(21)
+    counts = rng.multinomial(n_rows, rng.dirichlet(np.ones(n_groups)))
+    counts[[3, 17, 40]] = 0
+    counts[0] += n_rows - counts.sum()
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    offd = torch.as_tensor(off, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(21)
+    x = torch.randn(n_rows, n_cols, device=DEV, generator=g).to(torch.bfloat16)
+    cols = np.unique(np.concatenate([sample(n_cols, 6, 22), np.arange(8190, n_cols)]))
+    for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+        q = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_ROWS, True, MASK, U.GRID_UNIFORM, rnd, SEED, 1,
+                                group_offsets=offd)
+        assert q.kpad == U.padded_k_capacity(n_rows, n_groups)
+        r = torch.as_tensor(cols, device=DEV)
+        xb = O.to_blocked_rows(O.bf16_bits_to_f32(W.bits_numpy(x[:, r])), O.AXIS_ROWS, off)
+        if xb.shape[1] < q.kpad:
+            xb = np.concatenate([xb, np.zeros((xb.shape[0], q.kpad - xb.shape[1]), np.float32)], 1)
+        nib, s = O.quantize_blocked(xb, True, MASK, O.GRID_UNIFORM, rnd, SEED, 1, row_ids=cols)
+        assert np.array_equal(q.codes[r].cpu().numpy(), O.pack_nibbles(nib)), f"rnd={rnd} codes"
+        assert np.array_equal(q.scales[r].cpu().numpy().view(np.uint32), s.view(np.uint32))
+        _, qc = U.ufp4_rht_quantize_dual(x, (True, 0x1234, 0), (True, MASK, 1), rnd=rnd,
+                                         seed=SEED, group_offsets=offd)
+        assert torch.equal(qc.codes, q.codes) and torch.equal(qc.scales, q.scales)
+        del q, qc
