@@ -88,7 +88,7 @@ def test_column_wise_wide_tiles_ragged(ld_extra):
     tiles at the same size.  Ragged rows (16380) and a ragged last column tile
     (8200 = 32 * 256 + 8 columns), contiguous and strided rows; sampled output
     rows (input columns, the last tile's all included) bit-exact against the
-    oracle for both grids, RTNE and SR."""
+    oracle for the three grids, RTNE and SR."""
     n_rows, n_cols = 16380, 8200
     g = torch.Generator(device=DEV)
     g.manual_seed(11 + ld_extra)
@@ -97,7 +97,7 @@ def test_column_wise_wide_tiles_ragged(ld_extra):
     assert x.stride(0) == n_cols + ld_extra
     cols = np.unique(np.concatenate([sample(n_cols, 6, 3 + ld_extra),
                                      np.arange(8188, n_cols)])).astype(np.int64)
-    for grid in (U.GRID_UNIFORM, U.GRID_E2M1):
+    for grid in (U.GRID_UNIFORM, U.GRID_E2M1, U.GRID_E2M1_MAX2):
         for rnd in (U.ROUND_RTNE, U.ROUND_SR):
             q = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_ROWS, True, MASK, grid, rnd, SEED, SID)
             assert q.rows == n_cols and q.kpad == 16384
