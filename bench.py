@@ -1,10 +1,14 @@
 """Throughput of the UFP4 hot path on one MI355X.
 
-A step is one pass of the whole path over the dense 1.5B-model linear layer
-(tokens 8192, hidden 2048, FFN 8192): the six quantized operands of the UFP4
-recipe (X and W along H for FPROP; dY along F with stochastic rounding and W
-along F for DGRAD; dY and X along the tokens for WGRAD, dY with stochastic
-rounding) and the three block-scaled 4-bit GEMMs.  By default the operands
+A step is one pass of the whole path over one layer: the six quantized
+operands of the UFP4 recipe (X and W along H for FPROP; dY along F with
+stochastic rounding and W along F for DGRAD; dY and X along the tokens for
+WGRAD, dY with stochastic rounding) and the three block-scaled 4-bit GEMMs.
+By default the layer is the MoE-124B expert layer at one GPU's share (32
+resident experts, hidden 6144, expert FFN 2048, 65536 tokens routed top-8
+with Zipf(1.1) counts: 524288 expert rows), with the grouped GEMMs;
+`--workload dense-1.5b` runs the dense 1.5B-model linear layer (tokens 8192,
+hidden 2048, FFN 8192) and `moe-7.9b` the 7.9B expert layer.  The operands
 come from three dual-axis quantizations (one read of X, W and dY each, both
 of the tensor's operands out; bit-identical to the six single-axis calls,
 which `--quantizer single` runs instead).  Inputs are synthetic (seeded, see
@@ -15,9 +19,11 @@ Prints one JSON line.  `value` is the whole step's throughput in GEMM
 TFLOP/s (3 x 2*T*H*F FLOP per step over the wall time of the step, the
 quantizations included).  The step is captured once as a HIP graph and the
 timed steps are replays of it (checked bit-identical to the eager step
-first; `--eager` times eager launches instead); the quantizer and GEMM
-kernels are also reported on their own, timed with HIP events on the stream
-they run on in an eager pass.
+first; `--eager` times eager launches instead).  Each kernel is also timed on
+its own: an eager pass records HIP events around every launch, on the stream
+the library launches on, with 512 MiB written between launches (outside the
+event pairs) so that no launch finds its inputs in the 256 MB MALL; the
+reported durations are medians over the steps.
 """
 from __future__ import annotations
 
@@ -47,33 +53,49 @@ GEMM_PIPE_PEAK_TFLOPS = 32 * 32 * 16 * 2 / GEMM_UNIT_CYCLES * SIMDS * 2.4e9 / 1e
 BYTES_PER_QUANT_ELEM = 2.0 + 0.5 + 0.25
 BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 
-# HBM bytes per GEMM launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE
-# counters (averaged over the FPROP, DGRAD and WGRAD launches of one step),
-# each scaled by the factor that makes the same counter read the known size
-# of a plain 1 GiB device copy.  The figures hold for the GEMM source whose
-# SHA-256 is recorded with them; any other source reports null.
-GEMM_TRAFFIC = {
-    "dense-1.5B-fc1": {"sha256": "971bca1c094a61516f3dc45f695bf48dbc823b70fd1cbf4105645979e74b7054",
-                       "bytes_per_launch": 361901606},
+# HBM bytes from the rocprofv3 FETCH_SIZE and WRITE_SIZE counters, each
+# scaled by the factor that makes the same counter read the known size of a
+# plain 1 GiB device copy: per GEMM launch (averaged over the FPROP, DGRAD
+# and WGRAD launches of one step) and per step of quantizations.  A figure
+# holds for the sources whose SHA-256 is recorded with it; after any change to
+# them the bench reports null until the counters are taken again.
+TRAFFIC = {
+    "dense-1.5B-fc1": {
+        "gemm": {"sha256": "971bca1c094a61516f3dc45f695bf48dbc823b70fd1cbf4105645979e74b7054",
+                 "bytes_per_launch": 361901606},
+    },
 }
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
+QUANT_SOURCES = ("uniform_grid_fp4_amd/csrc/quantize.hip",
+                 "uniform_grid_fp4_amd/csrc/ufp4_device.h",
+                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
+MALL_FLUSH_BYTES = 512 << 20
 
 
-def gemm_source_sha256() -> str:
+def source_sha256(sources) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in GEMM_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def gemm_traffic(workload: str):
-    rec = GEMM_TRAFFIC.get(workload)
-    if rec is None or rec["sha256"] != gemm_source_sha256():
+def gemm_source_sha256() -> str:
+    return source_sha256(GEMM_SOURCES)
+
+
+def measured_traffic(workload: str, part: str):
+    """Counter-measured bytes of `part` ("gemm": per launch, "quantize": per
+    step) for the current sources, or None."""
+    rec = TRAFFIC.get(workload, {}).get(part)
+    if rec is None:
         return None
-    return rec["bytes_per_launch"]
+    srcs = GEMM_SOURCES if part == "gemm" else QUANT_SOURCES
+    if rec["sha256"] != source_sha256(srcs):
+        return None
+    return rec["bytes_per_launch"] if part == "gemm" else rec["bytes_per_step"]
 
 
 def parse():
@@ -90,12 +112,14 @@ def parse():
     ap.add_argument("--quantizer", default="dual", choices=["single", "dual"],
                     help="single: six single-axis quantizations per step; dual: three dual-axis "
                          "quantizations (one read of X, W and dY each, both operands out)")
-    ap.add_argument("--workload", default="dense-1.5b",
-                    choices=["dense-1.5b", "quant-sweep", "moe-7.9b", "moe-124b", "copy", "q1-outputs",
-                             "mfma-peak"],
-                    help="dense-1.5b: the timed step (default); quant-sweep: the 2^28-element "
-                         "quantizer sweep, one JSON line per case; moe-*: the expert layers "
-                         "(grouped GEMMs), one JSON line; copy: a plain 1 GiB device copy, the "
+    ap.add_argument("--workload", default="moe-124b",
+                    choices=["moe-124b", "dense-1.5b", "moe-7.9b", "quant-sweep", "copy",
+                             "q1-outputs", "mfma-peak"],
+                    help="moe-124b: the timed step on the MoE-124B expert layer, one GPU's "
+                         "share (default); dense-1.5b, moe-7.9b: the same step on the dense "
+                         "1.5B linear layer or the MoE-7.9B expert layer; quant-sweep: the "
+                         "2^28-element quantizer sweep, one JSON line per case; copy: a plain "
+                         "1 GiB device copy, the "
                          "streaming ceiling and the calibration run of the HBM traffic "
                          "counters; q1-outputs: GEMM-output SQNR of each recipe against the "
                          "unquantized product, one JSON line per GEMM; mfma-peak: measured "
@@ -119,12 +143,22 @@ class Step:
         self.dw = torch.empty((F, H), dtype=torch.float32, device=dev)
         self.q = {}
         self.seed = 1234
+        self.flush_buf = None
         self.run(None)   # allocates the quantized buffers once
+
+    def _start(self, ev, name):
+        """Record the start event of launch `name` (per-kernel timing pass),
+        after writing MALL_FLUSH_BYTES so the launch finds no input in the
+        MALL; the write is outside the event pair."""
+        if ev is None:
+            return
+        if self.flush_buf is not None:
+            self.flush_buf.fill_(len(name) & 0xFF)
+        ev[name][0].record()
 
     def quant(self, name, x, axis, mask, rnd, sid, ev):
         U = self.U
-        if ev is not None:
-            ev[name][0].record()
+        self._start(ev, name)
         q = U.ufp4_rht_quantize(x, axis, True, mask, U.GRID_UNIFORM, rnd, self.seed, sid,
                                 out=self.q.get(name))
         if ev is not None:
@@ -135,8 +169,7 @@ class Step:
     def quant2(self, name, x, rowwise, colwise, rnd, ev, **kw):
         """Both operands of x from one read (dual-axis quantizer)."""
         U = self.U
-        if ev is not None:
-            ev[name][0].record()
+        self._start(ev, name)
         prev = self.q.get(name, (None, None))
         q = U.ufp4_rht_quantize_dual(x, rowwise, colwise, grid=U.GRID_UNIFORM, rnd=rnd,
                                      seed=self.seed, out_rows=prev[0], out_cols=prev[1], **kw)
@@ -146,8 +179,7 @@ class Step:
         return q
 
     def gemm(self, name, fn, a, b, out, ev):
-        if ev is not None:
-            ev[name][0].record()
+        self._start(ev, name)
         fn(a, b, out=out)
         if ev is not None:
             ev[name][1].record()
@@ -201,47 +233,9 @@ class Step:
         return 2.0 * self.T * self.H * self.F
 
 
-def cpu_baseline(L, target_s: float):
-    """The oracle on the host, on a bounded sample of the same workload: it
-    quantizes a sample of rows of each operand and runs the FP64 GEMM on a
-    sample of output rows; the per-element and per-FLOP rates are scaled to a
-    whole step."""
-    import numpy as np
+def host_cpu_info():
+    """Host CPU model, os.cpu_count() and the BLAS/OpenMP thread pools."""
     from threadpoolctl import threadpool_info
-    from oracle import ufp4_oracle as O
-    from uniform_grid_fp4_amd import workloads as W
-
-    xb, wb, dyb = W.bits_numpy(L.x), W.bits_numpy(L.w), W.bits_numpy(L.dy)
-    mf, md, mw = L.masks
-    T, H, F = xb.shape[0], L.hidden, L.ffn
-    # quantizer rate: rows of X and dY, row-wise and column-wise, RTNE and SR
-    t0 = time.perf_counter()
-    n_el = 0
-    rows = np.arange(64)
-    for bits, axis, rnd in ((xb, 0, 0), (dyb, 0, 1), (xb, 1, 0), (dyb, 1, 1)):
-        c, s, kp = O.quantize(bits, axis, True, mf, O.GRID_UNIFORM, rnd, 1234, 0, out_rows=rows)
-        n_el += c.shape[0] * kp
-        if time.perf_counter() - t0 > target_s / 2:
-            break
-    tq = time.perf_counter() - t0
-    q_rate = n_el / tq
-    # GEMM rate: FPROP on sampled output rows (B = the whole quantized W)
-    cw, sw, _ = O.quantize(wb, 0, True, mf, O.GRID_UNIFORM, 0)
-    cx, sx, _ = O.quantize(xb, 0, True, mf, O.GRID_UNIFORM, 0, out_rows=np.arange(256))
-    t1 = time.perf_counter()
-    flops = 0.0
-    done = 0
-    while True:
-        r0 = done % 256
-        Cr, _ = O.gemm_tn_rows(cx, sx, cw, sw, np.arange(r0, r0 + 32))
-        flops += 2.0 * 32 * F * H
-        done += 32
-        if time.perf_counter() - t1 > target_s / 2:
-            break
-    tg = time.perf_counter() - t1
-    g_rate = flops / tg
-    elems_step = 2 * (T * H + F * H + T * F)
-    step_s = elems_step / q_rate + 3 * 2.0 * T * H * F / g_rate
     pools = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in pools] + [1])
     blas = ", ".join(f"{i.get('internal_api', '?')} x{i.get('num_threads', '?')}" for i in pools)
@@ -254,16 +248,73 @@ def cpu_baseline(L, target_s: float):
                     break
     except OSError:
         pass
+    return int(threads), model, blas
+
+
+def cpu_baseline(L, st, target_s: float):
+    """The oracle on the host, on a bounded sample of the same workload.
+
+    Quantizer: 64 sampled rows of X and dY quantized row-wise (RTNE and SR),
+    and the first 4096 token rows x 64 columns of X and dY quantized
+    column-wise (along the tokens); the oracle's elements per second are
+    scaled to the step's 2 x (T*H + E*F*H + T*F) quantized elements.  GEMM:
+    the FP64 FPROP of the first expert (or the dense layer) on 32-row samples
+    of its output rows, scaled to the step's 3 x 2*T*H*F FLOP.  Inputs are
+    copied to the host in slices only."""
+    import numpy as np
+    from oracle import ufp4_oracle as O
+    from uniform_grid_fp4_amd import workloads as W
+
+    mf, md, mw = L.masks
+    H, F = L.hidden, L.ffn
+    T = int(L.offsets[-1])
+    c0 = int(L.offsets[1] - L.offsets[0])          # rows of the first group
+    rows = np.arange(64)
+    xr, dyr = W.bits_numpy(L.x[:64]), W.bits_numpy(L.dy[:64])
+    tk = min(4096, c0)
+    xc, dyc = W.bits_numpy(L.x[:tk, :64]), W.bits_numpy(L.dy[:tk, :64])
+    t0 = time.perf_counter()
+    n_el = 0
+    for bits, axis, rnd in ((xr, 0, 0), (dyr, 0, 1), (xc, 1, 0), (dyc, 1, 1)):
+        c, s, kp = O.quantize(bits, axis, True, mf, O.GRID_UNIFORM, rnd, 1234, 0,
+                              out_rows=rows if axis == 0 else None)
+        n_el += c.shape[0] * kp
+        if time.perf_counter() - t0 > target_s / 2:
+            break
+    tq = time.perf_counter() - t0
+    q_rate = n_el / tq
+    # FP64 GEMM rate: FPROP of group 0 (B = that group's whole quantized W)
+    cw, sw, _ = O.quantize(W.bits_numpy(L.w[:F]), 0, True, mf, O.GRID_UNIFORM, 0)
+    nr = min(256, c0)
+    cx, sx, _ = O.quantize(W.bits_numpy(L.x[:nr]), 0, True, mf, O.GRID_UNIFORM, 0)
+    t1 = time.perf_counter()
+    flops = 0.0
+    done = 0
+    while True:
+        r0 = done % max(nr - 31, 1)
+        _ = O.gemm_tn_rows(cx, sx, cw, sw, np.arange(r0, min(r0 + 32, nr)))
+        flops += 2.0 * min(32, nr - r0) * F * H
+        done += 32
+        if time.perf_counter() - t1 > target_s / 2:
+            break
+    tg = time.perf_counter() - t1
+    g_rate = flops / tg
+    elems_step = 2 * sum(v for k, v in st.quant_elems().items() if k.endswith("_dual"))
+    step_flop = 3 * st.gemm_flops()
+    step_s = elems_step / q_rate + step_flop / g_rate
+    threads, model, blas = host_cpu_info()
     return {
-        "value": 3 * 2.0 * T * H * F / step_s / 1e12,
+        "value": step_flop / step_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle quantizer on {n_el} elements (64-row samples of X and dY, row- and "
-                   f"column-wise, RTNE and SR: {q_rate / 1e6:.2f} M elem/s) and FP64 FPROP on "
-                   f"{done} output rows ({g_rate / 1e9:.1f} GFLOP/s), scaled to one step "
-                   f"({step_s:.1f} s); host {model}, cpu_count={os.cpu_count()}, "
-                   f"thread pools: {blas or 'none'}"),
+        "sample": (f"oracle quantizer on {n_el} elements (64-row samples of X and dY row-wise, "
+                   f"{tk} token rows x 64 columns of X and dY column-wise; RTNE and SR: "
+                   f"{q_rate / 1e6:.2f} M elem/s) and FP64 FPROP of the first "
+                   f"{'expert' if L.experts > 1 else 'layer'} on {done} output rows "
+                   f"({g_rate / 1e9:.1f} GFLOP/s), scaled to one step of {elems_step:.3g} "
+                   f"quantized elements and {step_flop:.3g} FLOP ({step_s:.1f} s); host {model}, "
+                   f"cpu_count={os.cpu_count()}, thread pools: {blas or 'none'}"),
     }
 
 
@@ -281,8 +332,7 @@ class MoeStep(Step):
 
     def quant(self, name, x, axis, mask, rnd, sid, ev, **kw):
         U = self.U
-        if ev is not None:
-            ev[name][0].record()
+        self._start(ev, name)
         q = U.ufp4_rht_quantize(x, axis, True, mask, U.GRID_UNIFORM, rnd, self.seed, sid,
                                 out=self.q.get(name), **kw)
         if ev is not None:
@@ -291,8 +341,7 @@ class MoeStep(Step):
         return q
 
     def gemm(self, name, kind, a, b, out, ev):
-        if ev is not None:
-            ev[name][0].record()
+        self._start(ev, name)
         self.U.ufp4_grouped_gemm(kind, self.offd, a, b, out=out)
         if ev is not None:
             ev[name][1].record()
@@ -657,24 +706,14 @@ def main():
         st.run(None)
     torch.cuda.synchronize()
 
-    names = st.quant_names + Step.GEMMS
-    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for n in names} for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        st.run(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
-    ms_step_eager = ms_step
+    # Step time: the step captured once as a HIP graph (stream capture of the
+    # same library calls on the same buffers) and replayed back to back, no
+    # per-launch host work or gaps.  Each of three checking replays first has
+    # its outputs overwritten with NaN and must reproduce the eager step bit
+    # for bit.
+    ms_step_eager = None
     graph_checked = None
     if not args.eager:
-        # The step captured once as a HIP graph (stream capture of the same
-        # library calls on the same buffers) and replayed: no per-launch host
-        # work or gaps.  Each of three checking replays first has its outputs
-        # overwritten with NaN and must reproduce the eager step bit for bit.
         outs = st.outputs()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -689,6 +728,7 @@ def main():
             torch.cuda.synchronize()
             assert all(torch.equal(a, b) for a, b in zip(outs, ref)), \
                 "graph replay differs from the eager step"
+            del ref
         graph_checked = 3
         for _ in range(args.warmup):
             g.replay()
@@ -698,11 +738,38 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # Eager steps, back to back (also the step time with --eager).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        st.run(None)
+    torch.cuda.synchronize()
+    ms_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+    if args.eager:
+        ms_step = ms_step_eager
 
-    dur = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}
+    # Per-kernel durations: an eager pass with HIP events around every launch
+    # and MALL_FLUSH_BYTES written before each (outside the event pair), so
+    # every launch reads its inputs from HBM; medians over the steps.
+    names = st.quant_names + Step.GEMMS
+    st.flush_buf = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in names} for _ in range(args.steps)]
+    for k in range(args.steps):
+        st.run(evs[k])
+    torch.cuda.synchronize()
+    st.flush_buf = None
+
+    def median(v):
+        v = sorted(v)
+        n = len(v)
+        return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+    dur = {n: median([e[n][0].elapsed_time(e[n][1]) for e in evs]) for n in names}
     q_ms = sum(dur[n] for n in st.quant_names)
     qb = st.quant_bytes()
     q_bytes = sum(qb.values())
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     g_ms = sum(dur[n] for n in Step.GEMMS)
     g_flop = 3 * st.gemm_flops()
     gemm_avg_ms = g_ms / 3
@@ -710,6 +777,8 @@ def main():
     used_peak = mfma_peak_tflops(0)   # measured after the timed region
     mix_peak = instruction_mix_tflops()
     step_tflops = g_flop / (ms_step * 1e-3) / 1e12
+    gemm_traffic = measured_traffic(L.name, "gemm")
+    quant_traffic = measured_traffic(L.name, "quantize")
 
     out = {
         "metric": "RHT+UFP4 quantize GB/s (% HBM peak); UFP4 GEMM TFLOP/s (% MFMA peak)",
@@ -719,9 +788,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "timing": ("HIP graph replays of the captured step (%d checking replays bit-identical "
-                   "to the eager step); kernel durations from an eager pass with HIP events"
-                   % graph_checked) if graph_checked else "eager launches with HIP events",
+        "timing": (("HIP graph replays of the captured step (%d checking replays bit-identical "
+                    "to the eager step)" % graph_checked) if graph_checked
+                   else "eager launches") +
+                  "; per-kernel durations: medians of HIP events on the launch stream over an "
+                  "eager pass with %d MiB written before each launch (cold MALL)"
+                  % (MALL_FLUSH_BYTES >> 20),
         "ms_per_step_eager": round(ms_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -732,14 +804,15 @@ def main():
                    "ffn": st.F, "experts": L.experts,
                    "recipe": "UFP4: uniform grid, RHT-16 on all 3 GEMMs, SR on dY",
                    "block": 16, "scale": "fp32 absmax"},
-        "quantize": {"gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
-                     "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "quantize": {"gbs": round(q_gbs, 1),
+                     "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
                      "ms_per_step": round(q_ms, 4),
                      "per_call_ms": {n: round(dur[n], 4) for n in st.quant_names},
                      "per_call_gbs": {n: round(qb[n] / (dur[n] * 1e-3) / 1e9, 1)
                                       for n in st.quant_names},
                      "kernels": "dual-axis" if st.dual else "single-axis",
-                     "bytes_per_step": q_bytes},
+                     "bytes_per_step": q_bytes,
+                     "cache": "cold"},
         "gemm": {"tflops": round(gemm_tflops, 2),
                  "frac_fp8_mfma_peak": round(gemm_tflops / FP8_MFMA_PEAK_TFLOPS, 4),
                  "used_instruction": MFMA_KINDS[0],
@@ -757,10 +830,16 @@ def main():
                      "achieved": round(gemm_tflops, 2), "peak": FP8_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / FP8_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": gemm_traffic(L.name)},
+                     "traffic": gemm_traffic},
+        "roofline_quantize": {"kernel": ("ufp4::quant_dual_kernel" if st.dual
+                                         else "ufp4::quant_{rows_contig,cols}_kernel"),
+                              "bound": "hbm", "achieved": round(q_gbs, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                              "traffic": quant_traffic},
     }
-    if not args.no_cpu_baseline and args.workload == "dense-1.5b":
-        out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(L, st, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
