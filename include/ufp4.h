@@ -27,8 +27,12 @@
  *
  * Conventions for every entry point:
  *   - All buffer pointers are DEVICE pointers owned by the caller (the
- *     library never allocates, frees or synchronises, and keeps no mutable
- *     global state).  Descriptor structs are HOST memory read during the call.
+ *     library never allocates, frees or synchronises).  Descriptor structs
+ *     are HOST memory read during the call.  The only state the library
+ *     keeps is two host-side, write-once caches per device: the compute-unit
+ *     count the quantizers size their grids by, and a bit recording that the
+ *     GEMM kernels' dynamic-LDS attribute has been set; neither changes any
+ *     result.
  *   - Work is enqueued on `stream` and runs asynchronously; results are valid
  *     once the stream has reached that point.  A call enqueues kernel
  *     launches only (no copy, memset or allocation), so a sequence of calls
@@ -212,9 +216,17 @@ ufp4_status ufp4_dequantize(const ufp4_qtensor *q, int32_t inverse_rht, float *o
  *   DGRAD: A = dY [T, F] (blocks along F), B = W^T [H, F] (W quantized with
  *          ALONG_ROWS) -> dX [T, H]
  *   WGRAD: A = dY^T [F, T], B = X^T [H, T] (both ALONG_ROWS over tokens)
- *          -> dW [F, H].  workspace may be NULL (workspace_bytes 0); a
- *          workspace of ufp4_workspace_size(2, F, H, kpad, 1) bytes lets the
- *          call split K across workgroups (deterministic fixed-order sum). */
+ *          -> dW [F, H].  workspace may be NULL (workspace_bytes 0).  When
+ *          ufp4_workspace_size(2, F, H, kpad, 1) is non-zero and the
+ *          workspace (device, 4-byte aligned, contents ignored and
+ *          overwritten) holds at least that many bytes, the call splits K:
+ *          each split writes FP32 partial outputs into the workspace and a
+ *          second kernel sums them in split order into dW (deterministic;
+ *          equal to the unsplit result within the same tolerance, not bit
+ *          for bit).  A smaller workspace runs unsplit.  Returns OK,
+ *          INVALID_ARG (also: NULL workspace with a size, a size with no
+ *          workspace, a misaligned workspace), SHAPE, MISMATCH, UNSUPPORTED,
+ *          HIP. */
 ufp4_status ufp4_gemm_fprop(const ufp4_qtensor *xq, const ufp4_qtensor *wq, float *y,
                             int64_t ldy, hipStream_t stream);
 ufp4_status ufp4_gemm_dgrad(const ufp4_qtensor *dyq, const ufp4_qtensor *wtq, float *dx,
@@ -236,7 +248,12 @@ typedef enum { UFP4_OUT_F32 = 0, UFP4_OUT_BF16 = 1 } ufp4_out_dtype;
 ufp4_status ufp4_gemm_out(int32_t kind, const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
                           int32_t out_dtype, int64_t ldc, hipStream_t stream);
 
-/* ufp4_grouped_gemm -- the expert-grouped (MoE) form.
+/* ufp4_grouped_gemm -- the expert-grouped (MoE) form of the three training
+ * GEMMs, for the expert layers of the pages' MoE models (paperlayer.ai
+ * summary, section 5 "Q2-Q3: Long-run training and scaling": MoE 7.9B and
+ * 124B), with the RHT along each GEMM's contraction as in section 2 "Random
+ * Hadamard transforms" -- for WGRAD that is the tokens, so each expert's
+ * token run is padded and rotated on its own.
  * kind 0 (FPROP) / 1 (DGRAD): rows of A are split into n_groups groups by the
  *   device int64 offsets d_group_offsets[n_groups+1] (first 0, last a->rows);
  *   B stacks the groups' operands, b->rows = n_groups * N; group e computes
@@ -245,7 +262,9 @@ ufp4_status ufp4_gemm_out(int32_t kind, const ufp4_qtensor *a, const ufp4_qtenso
  *   quantized ALONG_ROWS with the same offsets (per-group padding, see
  *   ufp4_rht_quantize); C is [n_groups, M, N] with group stride M*ldc, and an
  *   empty group writes zeros.
- * workspace may be NULL.  Returns OK, INVALID_ARG, SHAPE, MISMATCH, HIP. */
+ * The grouped forms never split K (their per-group tiles fill the GPU), so
+ * the workspace is unused: pass NULL and 0 (a non-NULL workspace with a size
+ * is accepted and ignored).  Returns OK, INVALID_ARG, SHAPE, MISMATCH, HIP. */
 ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
                               const ufp4_qtensor *a, const ufp4_qtensor *b, float *c,
                               int64_t ldc, void *workspace, size_t workspace_bytes,
@@ -303,11 +322,16 @@ ufp4_status ufp4_output_stats(const float *ref, int64_t ld_ref, const float *tes
                               int64_t ld_test, int64_t rows, int64_t cols, void *workspace,
                               size_t workspace_bytes, ufp4_stats *d_out, hipStream_t stream);
 
-/* Bytes of workspace a GEMM call can use to split K (0 if it never does). */
+/* Bytes of workspace a GEMM call can use to split K: non-zero only for the
+ * dense WGRAD (kind 2, n_groups 1) of an M x N output whose 128 x 128 tiles
+ * number fewer than the 512 workgroups MI355X runs at once, with
+ * s = min(16, 512 / tiles, kpad / 1024) >= 2 splits: s * M * N * 4 bytes.
+ * 0 for every other kind, group count or invalid shape. */
 size_t ufp4_workspace_size(int32_t kind, int64_t m, int64_t n, int64_t kpad, int32_t n_groups);
 
-/* ufp4_grouped_gemm_out -- ufp4_grouped_gemm with the output element type
- * chosen by out_dtype (ufp4_out_dtype; ldc in elements) and no workspace. */
+/* ufp4_grouped_gemm_out -- ufp4_grouped_gemm (the MoE expert layers of
+ * paperlayer.ai section 5 "Q2-Q3") with the output element type chosen by
+ * out_dtype (ufp4_out_dtype; ldc in elements) and no workspace. */
 ufp4_status ufp4_grouped_gemm_out(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
                                   const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
                                   int32_t out_dtype, int64_t ldc, hipStream_t stream);

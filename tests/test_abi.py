@@ -239,3 +239,38 @@ def test_size_limits_of_32_bit_offsets():
     assert quant(axis=1, ld=(1 << 26) + 2, out=fake_desc(rows=32, kpad=32)) == -4
     big = fake_desc(k=(1 << 24) + 16, kpad=(1 << 24) + 16)
     assert gemm(U.lib().ufp4_gemm_fprop, big, big) == -4
+
+
+def test_workspace_size_splits_long_k_of_small_outputs():
+    """ufp4_workspace_size: FP32 partial outputs of the K splits of a dense
+    WGRAD whose 128x128 output tiles fill fewer than the 512 workgroups the GPU
+    runs at once; at most 16 splits of at least 64 blocks each; 0 otherwise."""
+    ws = U.ufp4_workspace_size
+    # 256 x 256 weight gradient over 149184 tokens (a MoE-124B expert's share):
+    # 4 tiles, min(16, 512 // 4, 9324 // 64) = 16 splits
+    assert ws(2, 256, 256, 149184, 1) == 16 * 256 * 256 * 4
+    # 1024 x 1024 over 8192 tokens: 64 tiles, min(16, 8, 512 // 64) = 8
+    assert ws(2, 1024, 1024, 8192, 1) == 8 * 1024 * 1024 * 4
+    # the dense 1.5B layer's dW (8192 x 2048 = 1024 tiles) fills the GPU
+    assert ws(2, 8192, 2048, 8192, 1) == 0
+    # short K: 2048 x 2048 over 1024 tokens (64 blocks) cannot split twice
+    assert ws(2, 2048, 2048, 1024, 1) == 0
+    # only the dense WGRAD splits; bad shapes need nothing
+    assert ws(0, 256, 256, 149184, 1) == 0 and ws(1, 256, 256, 149184, 1) == 0
+    assert ws(2, 256, 256, 149184, 4) == 0
+    assert ws(2, 0, 256, 4096, 1) == 0 and ws(2, 256, 256, 4008, 1) == 0
+
+
+def test_wgrad_workspace_arguments():
+    L = U.lib()
+    a, b = fake_desc(), fake_desc()
+    # NULL workspace with a size, a size-0 workspace, a misaligned workspace
+    assert L.ufp4_gemm_wgrad(ctypes.byref(a), ctypes.byref(b), FAKE, 32, None, 64, None) == -1
+    assert L.ufp4_gemm_wgrad(ctypes.byref(a), ctypes.byref(b), FAKE, 32,
+                             ctypes.c_void_p(0x20000), 0, None) == -1
+    assert L.ufp4_gemm_wgrad(ctypes.byref(a), ctypes.byref(b), FAKE, 32,
+                             ctypes.c_void_p(0x20002), 64, None) == -1
+    # operand validation still comes first with a valid workspace
+    bad = fake_desc(kpad=48)
+    assert L.ufp4_gemm_wgrad(ctypes.byref(a), ctypes.byref(bad), FAKE, 32,
+                             ctypes.c_void_p(0x20000), 64, None) == -3

@@ -1,16 +1,53 @@
 """The linear and MoE expert layer wrappers: forward and backward equal the
 explicit sequence of C-ABI calls bit for bit (dual-axis quantizations with
-the layer's masks and SR seed, GEMMs with the bf16 epilogue), and stay within
-4-bit quantization noise of the unquantized product."""
+the layer's masks and SR seed, GEMMs with the bf16 epilogue), match the
+oracle element by element (its quantizer on the same bf16 inputs, masks and
+SR seed, then its FP64 GEMMs: |out - C| <= 1e-5 * sum_k |a_k||b_k| plus half a
+bf16 ulp of the output for the epilogue's rounding), and stay within 4-bit
+quantization noise of the unquantized product.  The recipe the layers follow
+is the paperlayer.ai summary's section 4 "UFP4 Recipe" (RHT on all three
+GEMMs along their contraction dimensions, stochastic rounding on dY only)."""
 import numpy as np
 import pytest
 import torch
 
+from oracle import ufp4_oracle as O
 from uniform_grid_fp4_amd import ufp4 as U
+from uniform_grid_fp4_amd import workloads as W
 from uniform_grid_fp4_amd.layers import UFP4ExpertLinear, UFP4Linear
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+TOL = 1e-5
+
+
+def assert_bf16_close(out, C, bound, what):
+    """out: bf16 GEMM output (the FP32 result v rounded to nearest even);
+    C, bound: the oracle's FP64 product and sum |a||b|.  |v - C| <= TOL*bound,
+    and the rounding adds at most half a bf16 ulp of v, <= 2^-8 |v|."""
+    o = out.detach().float().cpu().numpy().astype(np.float64)
+    lim = TOL * bound + 2.0 ** -8 * (np.abs(C) + TOL * bound)
+    err = np.abs(o - C)
+    bad = err > lim
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside, worst ratio "
+                           f"{(err / np.maximum(lim, 1e-300)).max():.3g}")
+
+
+def oracle_linear(x, w, g, masks, seed, grid=O.GRID_UNIFORM):
+    """The oracle's three GEMMs of a linear layer: the six quantized operands
+    (X and W along H, dY along F with SR stream 0, W^T along F, dY^T with SR
+    stream 1 and X^T along the tokens) and FP64 products."""
+    mf, md, mw = masks
+    xb, wb, gb = W.bits_numpy(x), W.bits_numpy(w), W.bits_numpy(g)
+    q = lambda b, axis, mask, rnd=0, sid=0: O.quantize(b, axis, True, mask, grid, rnd, seed, sid)
+    cx, sx, _ = q(xb, O.AXIS_COLS, mf)
+    cw, sw, _ = q(wb, O.AXIS_COLS, mf)
+    cg, sg, _ = q(gb, O.AXIS_COLS, md, 1, 0)
+    cwt, swt, _ = q(wb, O.AXIS_ROWS, md)
+    cgt, sgt, _ = q(gb, O.AXIS_ROWS, mw, 1, 1)
+    cxt, sxt, _ = q(xb, O.AXIS_ROWS, mw)
+    return (O.gemm_tn(cx, sx, cw, sw, grid), O.gemm_tn(cg, sg, cwt, swt, grid),
+            O.gemm_tn(cgt, sgt, cxt, sxt, grid))
 
 
 def rel_rms(a, b):
@@ -36,6 +73,11 @@ def test_linear_layer():
     assert torch.equal(y.reshape(-1, 384), U.ufp4_gemm_out(U.FPROP, xq, wq))
     assert torch.equal(x.grad.reshape(-1, 256), U.ufp4_gemm_out(U.DGRAD, dq, wtq))
     assert torch.equal(layer.weight.grad, U.ufp4_gemm_out(U.WGRAD, dtq, xtq))
+    # the oracle, element by element, on the same inputs, masks and SR seed
+    (Cy, By), (Cdx, Bdx), (Cdw, Bdw) = oracle_linear(x2, w, g2, layer.masks, layer.sr_seed)
+    assert_bf16_close(y.reshape(-1, 384), Cy, By, "linear fprop")
+    assert_bf16_close(x.grad.reshape(-1, 256), Cdx, Bdx, "linear dgrad")
+    assert_bf16_close(layer.weight.grad, Cdw, Bdw, "linear wgrad")
     # and it is the product it stands for, up to 4-bit noise
     xf, wf, gf = x2.float(), w.float(), g2.float()
     assert rel_rms(y.reshape(-1, 384), xf @ wf.t()) < 0.2
@@ -77,7 +119,28 @@ def test_expert_layer():
     dw = U.ufp4_grouped_gemm_out(U.WGRAD, off, dtq, xtq).reshape(E * F, H)
     assert torch.equal(layer.weight.grad, dw)
     assert (layer.weight.grad[F:2 * F] == 0).all()            # the expert with no tokens
+    # the oracle, element by element: grouped quantizations (per-expert
+    # padding along the tokens, stacked per-expert W^T) and grouped FP64 GEMMs
     o = off.tolist()
+    xb, wb, gb = W.bits_numpy(x.detach()), W.bits_numpy(w), W.bits_numpy(g)
+    seed, grid = layer.sr_seed, O.GRID_UNIFORM
+    kp = U.padded_k_capacity(T, E)
+    q = lambda b, axis, mask, rnd=0, sid=0, **kw: O.quantize(b, axis, True, mask, grid, rnd,
+                                                             seed, sid, **kw)
+    cx, sx, _ = q(xb, O.AXIS_COLS, mf)
+    cw, sw, _ = q(wb, O.AXIS_COLS, mf)
+    cg, sg, _ = q(gb, O.AXIS_COLS, md, 1, 0)
+    cwt, swt, _ = q(wb, O.AXIS_ROWS_STACKED, md, n_stack=E)
+    cgt, sgt, _ = q(gb, O.AXIS_ROWS, mw, 1, 1, group_offsets=o, kpad=kp)
+    cxt, sxt, _ = q(xb, O.AXIS_ROWS, mw, group_offsets=o, kpad=kp)
+    Cy, By = O.grouped_gemm(0, o, cx, sx, cw, sw, F, grid)
+    Cdx, Bdx = O.grouped_gemm(1, o, cg, sg, cwt, swt, H, grid)
+    Cdw, Bdw = O.grouped_gemm(2, o, cgt, sgt, cxt, sxt, H, grid)
+    assert_bf16_close(y, Cy, By, "expert fprop")
+    assert_bf16_close(x.grad, Cdx, Bdx, "expert dgrad")
+    assert_bf16_close(layer.weight.grad, Cdw.reshape(E * F, H), Bdw.reshape(E * F, H),
+                      "expert wgrad")
+    assert not Cdw[1].any()
     for e in range(E):
         if counts[e] == 0:
             continue

@@ -80,6 +80,28 @@ def test_sweep_dual_quantizer_full_size(sweep):
                   mask=0x1234, what=f"{dist} dual column-wise")
 
 
+@pytest.mark.parametrize("rnd", [U.ROUND_RTNE, U.ROUND_SR])
+def test_sweep_single_and_dual_agree_whole_output(sweep, rnd):
+    """Every code and scale of the full 16384 x 16384 outputs, not a sample:
+    the column-wise single-axis call (four columns per lane, its XCD-major
+    tile order) equals the dual-axis kernel's column-wise output (two columns
+    per lane, its own tiles), and the row-wise single-axis call equals the
+    dual-axis kernel's row-wise output, for RTNE and SR (same masks, seed and
+    streams).  The oracle pins sampled rows of both in the tests above."""
+    dist, x = sweep
+    q_r, q_c = U.ufp4_rht_quantize_dual(x, (True, MASK, 0), (True, 0x1234, 1),
+                                        grid=U.GRID_UNIFORM, rnd=rnd, seed=SEED)
+    s_c = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_ROWS, True, 0x1234, U.GRID_UNIFORM, rnd, SEED, 1)
+    assert torch.equal(s_c.codes, q_c.codes), f"{dist} rnd={rnd}: column-wise codes"
+    assert torch.equal(s_c.scales.view(torch.int32), q_c.scales.view(torch.int32))
+    del s_c
+    s_r = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_COLS, True, MASK, U.GRID_UNIFORM, rnd, SEED, 0)
+    assert torch.equal(s_r.codes, q_r.codes), f"{dist} rnd={rnd}: row-wise codes"
+    assert torch.equal(s_r.scales.view(torch.int32), q_r.scales.view(torch.int32))
+    del s_r, q_r, q_c
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("ld_extra", [0, 8, 2])
 def test_column_wise_wide_tiles_ragged(ld_extra):
     """Large column-wise inputs take the kernel's four-columns-per-lane tiles

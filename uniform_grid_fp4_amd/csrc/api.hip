@@ -44,8 +44,16 @@ ufp4_status check_pair(const ufp4_qtensor *a, const ufp4_qtensor *b) {
   return UFP4_OK;
 }
 
+// Workspace bytes of a dense GEMM's split-K (0: it does not split).
+size_t split_workspace_bytes(int64_t m, int64_t n, int64_t kpad) {
+  if (m <= 0 || n <= 0 || kpad <= 0 || kpad % 16 != 0) return 0;
+  const int splits = gemm_splits(m, n, kpad);
+  return splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+// Dense GEMM; with `ws` (FP32, at least split_workspace_bytes) K is split.
 ufp4_status dense_gemm(const ufp4_qtensor *a, const ufp4_qtensor *b, void *c, int out_bf16,
-                       int64_t ldc, hipStream_t stream) {
+                       int64_t ldc, hipStream_t stream, float *ws = nullptr) {
   ufp4_status s = check_pair(a, b);
   if (s != UFP4_OK) return s;
   if (c == nullptr) return UFP4_ERR_INVALID_ARG;
@@ -66,6 +74,14 @@ ufp4_status dense_gemm(const ufp4_qtensor *a, const ufp4_qtensor *b, void *c, in
   g.goff = nullptr;
   g.n_groups = 1;
   g.grid = a->grid;
+  g.n_split = 1;
+  g.split_kb = a->kpad / 16;
+  g.split_stride = 0;
+  if (ws != nullptr && !out_bf16) {
+    g.n_split = gemm_splits(g.M, g.N, g.kpad);
+    if (g.n_split > 1) return launch_gemm_split(g, ws, stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
+    g.n_split = 1;
+  }
   return launch_gemm(g, stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
 }
 
@@ -241,7 +257,14 @@ ufp4_status ufp4_gemm_wgrad(const ufp4_qtensor *dytq, const ufp4_qtensor *xtq, f
                             int64_t lddw, void *workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   if ((workspace == nullptr) != (workspace_bytes == 0)) return UFP4_ERR_INVALID_ARG;
-  return dense_gemm(dytq, xtq, dw, 0, lddw, stream);
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
+    return UFP4_ERR_INVALID_ARG;
+  float *ws = nullptr;
+  if (workspace != nullptr && dytq != nullptr && xtq != nullptr) {
+    const size_t need = split_workspace_bytes(dytq->rows, xtq->rows, dytq->kpad);
+    if (need > 0 && workspace_bytes >= need) ws = static_cast<float *>(workspace);
+  }
+  return dense_gemm(dytq, xtq, dw, 0, lddw, stream, ws);
 }
 
 ufp4_status ufp4_gemm_out(int32_t kind, const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
@@ -282,6 +305,9 @@ ufp4_status ufp4_grouped_gemm_out(int32_t kind, int32_t n_groups, const int64_t 
   g.goff = d_group_offsets;
   g.n_groups = n_groups;
   g.grid = a->grid;
+  g.n_split = 1;
+  g.split_kb = a->kpad / 16;
+  g.split_stride = 0;
   g.M = a->rows;
   if (kind == 2) {
     g.mode = 2;
@@ -347,12 +373,8 @@ ufp4_status ufp4_output_stats(const float *ref, int64_t ld_ref, const float *tes
 }
 
 size_t ufp4_workspace_size(int32_t kind, int64_t m, int64_t n, int64_t kpad, int32_t n_groups) {
-  (void)kind;
-  (void)m;
-  (void)n;
-  (void)kpad;
-  (void)n_groups;
-  return 0;
+  if (kind != 2 || n_groups != 1) return 0;
+  return split_workspace_bytes(m, n, kpad);
 }
 
 const char *ufp4_status_string(ufp4_status status) {

@@ -396,7 +396,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   if (MODE != 0) load_gemm_groups<MODE>(g, s_off, s_pre, s_scan, s_order);
 
   int64_t total;
-  if (MODE == 0) total = tiles_m * tiles_n;
+  if (MODE == 0) total = tiles_m * tiles_n * g.n_split;
   else if (MODE == 1) total = s_pre[g.n_groups];
   else total = (int64_t)g.n_groups * tiles_m * tiles_n;
   // Dense and M-grouped tiles all cost the same K, so each XCD takes a
@@ -416,15 +416,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   for (int64_t t = t_first; t < t_end; t += t_step) {
     TileJob job;
     if (MODE == 0) {
+      // split-K: tile t of split s covers blocks [s * split_kb, ...) and
+      // writes its partial sums at s * split_stride
+      const int64_t tiles = tiles_m * tiles_n;
+      int64_t sp = 0, local = t;
+      while (local >= tiles) {   // at most kMaxSplits - 1 steps, no 64-bit division
+        local -= tiles;
+        ++sp;
+      }
       int64_t tm, tn;
-      band_tile(t, tiles_m, tiles_n, tm, tn);
+      band_tile(local, tiles_m, tiles_n, tm, tn);
       job.a_row0 = tm * kBM;
       job.a_rows = min((int64_t)kBM, g.M - job.a_row0);
       job.b_row0 = tn * kBN;
       job.b_rows = min((int64_t)kBN, g.N - job.b_row0);
-      job.kb0 = 0;
-      job.kb1 = kblocks;
-      job.c_off = job.a_row0 * g.ldc + job.b_row0;
+      job.kb0 = min(sp * g.split_kb, kblocks);
+      job.kb1 = min(job.kb0 + g.split_kb, kblocks);
+      job.c_off = sp * g.split_stride + job.a_row0 * g.ldc + job.b_row0;
     } else if (MODE == 1) {
       int lo = 0, hi = g.n_groups;   // largest e with s_pre[e] <= t
       while (hi - lo > 1) {
@@ -501,11 +509,53 @@ static hipError_t launch_t(const GemmArgs &g, int64_t blocks, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Deterministic split-K sum: c[m, n] = sum over s = 0, 1, ... of the
+// partial outputs ws[s][m][n] (FP32 adds in that fixed order).
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ ws,
+                                                         int n_split, int64_t M, int64_t N,
+                                                         int64_t stride, float *__restrict__ c,
+                                                         int64_t ldc) {
+  const int64_t total = M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / N, n = i - m * N;
+    float acc = ws[i];
+    for (int sp = 1; sp < n_split; ++sp) acc += ws[sp * stride + i];
+    __builtin_nontemporal_store(acc, c + m * ldc + n);
+  }
+}
+
+int gemm_splits(int64_t M, int64_t N, int64_t kpad) {
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  int64_t s = kSplitSlots / (tiles > 0 ? tiles : 1);
+  if (s > kMaxSplits) s = kMaxSplits;
+  const int64_t by_k = (kpad / 16) / kMinSplitBlocks;
+  if (s > by_k) s = by_k;
+  return s >= 2 ? (int)s : 1;
+}
+
+hipError_t launch_gemm_split(const GemmArgs &g, float *ws, hipStream_t st) {
+  GemmArgs p = g;
+  const int64_t kblocks = g.kpad / 16;
+  p.c = ws;
+  p.ldc = g.N;
+  p.out_bf16 = 0;
+  p.split_kb = (kblocks + g.n_split - 1) / g.n_split;
+  p.split_stride = g.M * g.N;
+  hipError_t e = launch_gemm(p, st);
+  if (e != hipSuccess) return e;
+  int64_t blocks = (g.M * g.N + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ws, g.n_split,
+                     g.M, g.N, p.split_stride, static_cast<float *>(g.c), g.ldc);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
   const int64_t tiles_m = (g.M + kBM - 1) / kBM;
   const int64_t tiles_n = (g.N + kBN - 1) / kBN;
   int64_t total;
-  if (g.mode == 0) total = tiles_m * tiles_n;
+  if (g.mode == 0) total = tiles_m * tiles_n * g.n_split;
   else if (g.mode == 1) total = (tiles_m + g.n_groups) * tiles_n;   // upper bound
   else total = (int64_t)g.n_groups * tiles_m * tiles_n;
   int64_t blocks = total < 1 ? 1 : total;

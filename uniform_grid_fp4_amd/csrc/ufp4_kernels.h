@@ -96,8 +96,22 @@ struct GemmArgs {
   const int64_t *goff;
   int n_groups;
   int grid;
+  // mode 0 split-K: n_split > 1 splits the blocks into runs of split_kb, and
+  // split s writes its partial output at c + s * split_stride
+  int n_split;
+  int64_t split_kb;
+  int64_t split_stride;
 };
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
+
+// Split-K of a dense GEMM whose output tiles do not fill the GPU: partial
+// outputs of the K splits in the FP32 workspace ws [n_split, M, N], then a
+// fixed-order sum into g.c (FP32, row stride g.ldc).
+constexpr int kSplitSlots = 512;      // workgroups the GPU runs at once (2 per CU, 256 CUs)
+constexpr int kMaxSplits = 16;
+constexpr int kMinSplitBlocks = 64;   // at least 1024 of K per split
+int gemm_splits(int64_t M, int64_t N, int64_t kpad);
+hipError_t launch_gemm_split(const GemmArgs &g, float *ws, hipStream_t st);
 
 }  // namespace ufp4
