@@ -313,6 +313,23 @@ ufp4_status ufp4_quant_stats(const uint16_t *x_bf16, int64_t n_rows, int64_t n_c
                              int32_t axis, const ufp4_qtensor *q, void *workspace,
                              size_t workspace_bytes, ufp4_stats *d_out, hipStream_t stream);
 
+/* ufp4_quant_stats_noalloc -- ufp4_quant_stats without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * (minus workspace and workspace_bytes), checks and results, bit for bit:
+ * the partial sums go to a scratch array the library holds in device memory,
+ * 1024 records of 192 bytes (192 KiB) per GPU, taken on the first call on
+ * each device and kept until the process ends.  The diagnostics kernels use
+ * at most 1024 partial records for any input size, so no input exceeds it;
+ * nothing is allocated, freed or cleared by the call.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and may return wrong
+ * sums -- order them on one stream.  Returns OK, INVALID_ARG, SHAPE, HIP (also
+ * when the scratch array's address cannot be obtained). */
+ufp4_status ufp4_quant_stats_noalloc(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols,
+                                     int64_t ld, int32_t axis, const ufp4_qtensor *q,
+                                     ufp4_stats *d_out, hipStream_t stream);
+
 /* ufp4_output_stats -- the same sums for a GEMM output `test` [rows, cols]
  * (stride ld_test) against a reference output `ref` (stride ld_ref), FP32
  * device arrays: x = ref, xhat = test; n_nonzero, n_underflow and hist are 0.

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     decl = declared_functions()
-    assert len(decl) == 14, decl
+    assert len(decl) == 15, decl
     assert sorted(U.EXPORTS) == decl
     L = U.lib()
     for name in decl:
@@ -274,3 +274,20 @@ def test_wgrad_workspace_arguments():
     bad = fake_desc(kpad=48)
     assert L.ufp4_gemm_wgrad(ctypes.byref(a), ctypes.byref(bad), FAKE, 32,
                              ctypes.c_void_p(0x20000), 64, None) == -3
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), -1), (dict(out=None), -1), (dict(out=ctypes.c_void_p(0x30004)), -1),
+    (dict(axis=2), -1), (dict(axis=7), -1),
+    (dict(q=fake_desc(rows=32, k=48, kpad=64)), -2),
+    (dict(q=fake_desc(rows=31, k=48, kpad=48)), -2),
+    (dict(axis=1), -2), (dict(ld=40), -2), (dict(n_rows=0), -2),
+])
+def test_quant_stats_noalloc_rejects(kw, expect):
+    """The no-allocation diagnostics call validates exactly as
+    ufp4_quant_stats (it has no workspace to check) before touching the GPU."""
+    a = dict(x=FAKE, n_rows=32, n_cols=48, ld=48, axis=0, q=fake_desc(rows=32, k=48, kpad=48),
+             out=ctypes.c_void_p(0x30000))
+    a.update(kw)
+    assert U.lib().ufp4_quant_stats_noalloc(a["x"], a["n_rows"], a["n_cols"], a["ld"], a["axis"],
+                                            ctypes.byref(a["q"]), a["out"], None) == expect

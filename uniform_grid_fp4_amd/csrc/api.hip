@@ -144,6 +144,36 @@ void fill_quant_desc(ufp4_qtensor *out, int64_t n_rows, int64_t n_cols, int32_t 
   out->sign_mask = rht ? sign_mask : 0u;
 }
 
+// Checks of a quantization-diagnostics call (workspace aside) and its
+// kernel arguments.
+ufp4_status quant_stats_args(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
+                             int32_t axis, const ufp4_qtensor *q, const ufp4_stats *d_out,
+                             StatsArgs &a) {
+  ufp4_status s = check_qtensor(q);
+  if (s != UFP4_OK) return s;
+  if (x_bf16 == nullptr || d_out == nullptr) return UFP4_ERR_INVALID_ARG;
+  if (!aligned8(d_out)) return UFP4_ERR_INVALID_ARG;
+  if (axis != UFP4_BLOCKS_ALONG_COLS && axis != UFP4_BLOCKS_ALONG_ROWS)
+    return UFP4_ERR_INVALID_ARG;
+  if (n_rows <= 0 || n_cols <= 0 || ld < n_cols) return UFP4_ERR_SHAPE;
+  const int64_t rows = axis == UFP4_BLOCKS_ALONG_COLS ? n_rows : n_cols;
+  const int64_t k = axis == UFP4_BLOCKS_ALONG_COLS ? n_cols : n_rows;
+  if (q->rows != rows || q->k != k || q->kpad != round_up16(k)) return UFP4_ERR_SHAPE;
+  a = StatsArgs{};
+  a.x = x_bf16;
+  a.ld = ld;
+  a.axis = axis;
+  a.rows = rows;
+  a.kpad = q->kpad;
+  a.kvalid = k;
+  a.codes = q->codes;
+  a.scales = q->scales;
+  a.grid = q->grid;
+  a.rht = q->rht;
+  a.sign_mask = q->rht ? q->sign_mask : 0u;
+  return UFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -328,31 +358,25 @@ size_t ufp4_stats_workspace_size(void) { return (size_t)kStatsMaxBlocks * sizeof
 ufp4_status ufp4_quant_stats(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols, int64_t ld,
                              int32_t axis, const ufp4_qtensor *q, void *workspace,
                              size_t workspace_bytes, ufp4_stats *d_out, hipStream_t stream) {
-  ufp4_status s = check_qtensor(q);
+  StatsArgs a;
+  const ufp4_status s = quant_stats_args(x_bf16, n_rows, n_cols, ld, axis, q, d_out, a);
   if (s != UFP4_OK) return s;
-  if (x_bf16 == nullptr || workspace == nullptr || d_out == nullptr) return UFP4_ERR_INVALID_ARG;
-  if (!aligned8(workspace) || !aligned8(d_out)) return UFP4_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned8(workspace)) return UFP4_ERR_INVALID_ARG;
   if (workspace_bytes < ufp4_stats_workspace_size()) return UFP4_ERR_INVALID_ARG;
-  if (axis != UFP4_BLOCKS_ALONG_COLS && axis != UFP4_BLOCKS_ALONG_ROWS)
-    return UFP4_ERR_INVALID_ARG;
-  if (n_rows <= 0 || n_cols <= 0 || ld < n_cols) return UFP4_ERR_SHAPE;
-  const int64_t rows = axis == UFP4_BLOCKS_ALONG_COLS ? n_rows : n_cols;
-  const int64_t k = axis == UFP4_BLOCKS_ALONG_COLS ? n_cols : n_rows;
-  if (q->rows != rows || q->k != k || q->kpad != round_up16(k)) return UFP4_ERR_SHAPE;
-  StatsArgs a{};
-  a.x = x_bf16;
-  a.ld = ld;
-  a.axis = axis;
-  a.rows = rows;
-  a.kpad = q->kpad;
-  a.kvalid = k;
-  a.codes = q->codes;
-  a.scales = q->scales;
-  a.grid = q->grid;
-  a.rht = q->rht;
-  a.sign_mask = q->rht ? q->sign_mask : 0u;
   return launch_quant_stats(a, static_cast<StatsPartial *>(workspace),
                             reinterpret_cast<StatsPartial *>(d_out), stream) == hipSuccess
+             ? UFP4_OK
+             : UFP4_ERR_HIP;
+}
+
+ufp4_status ufp4_quant_stats_noalloc(const uint16_t *x_bf16, int64_t n_rows, int64_t n_cols,
+                                     int64_t ld, int32_t axis, const ufp4_qtensor *q,
+                                     ufp4_stats *d_out, hipStream_t stream) {
+  StatsArgs a;
+  const ufp4_status s = quant_stats_args(x_bf16, n_rows, n_cols, ld, axis, q, d_out, a);
+  if (s != UFP4_OK) return s;
+  return launch_quant_stats_scratch(a, reinterpret_cast<StatsPartial *>(d_out), stream) ==
+                 hipSuccess
              ? UFP4_OK
              : UFP4_ERR_HIP;
 }

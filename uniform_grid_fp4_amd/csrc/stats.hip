@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "ufp4_device.h"
 #include "ufp4_kernels.h"
 
@@ -253,6 +255,48 @@ hipError_t launch_quant_stats(const StatsArgs &a, StatsPartial *workspace, Stats
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kStatsThreads), 0, st, workspace, blocks,
                      out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation diagnostics call: the kStatsMaxBlocks partial
+// records (192 KiB) in device memory the library itself owns.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` only stands in for the symbol; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept below, and only that address reaches kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) StatsPartial scratch[kStatsMaxBlocks];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<StatsPartial *> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device; concurrent first calls store the same address).
+static hipError_t scratch_address(StatsPartial **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  StatsPartial *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void *addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<StatsPartial *>(addr);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_quant_stats_scratch(const StatsArgs &a, StatsPartial *out, hipStream_t st) {
+  // the grid (one partial per workgroup) never exceeds the array
+  if (stats_grid(a.rows * (a.kpad / 16)) > kStatsMaxBlocks) return hipErrorInvalidValue;
+  StatsPartial *ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_quant_stats(a, ws, out, st);
 }
 
 hipError_t launch_output_stats(const float *ref, int64_t ld_ref, const float *test,

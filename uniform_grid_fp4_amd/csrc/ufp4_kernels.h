@@ -75,6 +75,9 @@ struct StatsArgs {
 
 hipError_t launch_quant_stats(const StatsArgs &a, StatsPartial *workspace, StatsPartial *out,
                               hipStream_t st);
+// The same with the partials in the library's own per-device scratch array
+// (no workspace argument, no allocation).
+hipError_t launch_quant_stats_scratch(const StatsArgs &a, StatsPartial *out, hipStream_t st);
 hipError_t launch_output_stats(const float *ref, int64_t ld_ref, const float *test,
                                int64_t ld_test, int64_t rows, int64_t cols,
                                StatsPartial *workspace, StatsPartial *out, hipStream_t st);

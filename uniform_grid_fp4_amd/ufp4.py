@@ -30,7 +30,8 @@ STATUS = {0: "UFP4_OK", -1: "UFP4_ERR_INVALID_ARG", -2: "UFP4_ERR_SHAPE",
 EXPORTS = ("ufp4_rht_quantize", "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop",
            "ufp4_gemm_dgrad", "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_workspace_size",
            "ufp4_status_string", "ufp4_stats_workspace_size", "ufp4_quant_stats",
-           "ufp4_output_stats", "ufp4_gemm_out", "ufp4_grouped_gemm_out")
+           "ufp4_output_stats", "ufp4_gemm_out", "ufp4_grouped_gemm_out",
+           "ufp4_quant_stats_noalloc")
 
 
 class UFP4Error(RuntimeError):
@@ -86,9 +87,11 @@ def lib() -> ctypes.CDLL:
     L.ufp4_stats_workspace_size.restype = ctypes.c_size_t
     L.ufp4_quant_stats.argtypes = [P, I64, I64, I64, I32, Q, P, ctypes.c_size_t, P, P]
     L.ufp4_output_stats.argtypes = [P, I64, P, I64, I64, I64, P, ctypes.c_size_t, P, P]
+    L.ufp4_quant_stats_noalloc.argtypes = [P, I64, I64, I64, I32, Q, P, P]
     L.ufp4_status_string.argtypes = [I32]
     L.ufp4_status_string.restype = ctypes.c_char_p
-    for f in ("ufp4_quant_stats", "ufp4_output_stats", "ufp4_rht_quantize",
+    for f in ("ufp4_quant_stats", "ufp4_quant_stats_noalloc", "ufp4_output_stats",
+              "ufp4_rht_quantize",
               "ufp4_rht_quantize_dual", "ufp4_dequantize", "ufp4_gemm_fprop", "ufp4_gemm_dgrad",
               "ufp4_gemm_wgrad", "ufp4_grouped_gemm", "ufp4_gemm_out", "ufp4_grouped_gemm_out"):
         getattr(L, f).restype = ctypes.c_int32
@@ -243,6 +246,23 @@ def ufp4_quant_stats(x: torch.Tensor, q: Quantized, axis: int = BLOCKS_ALONG_COL
     st = lib().ufp4_quant_stats(_ptr(x), x.shape[0], x.shape[1], x.stride(0), axis,
                                 ctypes.byref(d), _ptr(ws), nbytes, _ptr(out), _stream(x.device))
     _check(st, "ufp4_quant_stats")
+    return _stats_dict(out)
+
+
+def ufp4_quant_stats_noalloc(x: torch.Tensor, q: Quantized, axis: int = BLOCKS_ALONG_COLS,
+                             out: Optional[torch.Tensor] = None) -> dict:
+    """ufp4_quant_stats with the partial sums in the library's own scratch
+    array (the C call takes no workspace and allocates nothing); `out`, an
+    int64 tensor of 24 elements, receives the ufp4_stats record.  Waits for
+    the result."""
+    assert x.dim() == 2 and x.dtype == torch.bfloat16 and x.is_cuda and x.stride(1) == 1
+    if out is None:
+        out = torch.empty(24, dtype=torch.int64, device=x.device)
+    assert out.dtype == torch.int64 and out.numel() == 24 and out.is_contiguous()
+    d = q.desc()
+    st = lib().ufp4_quant_stats_noalloc(_ptr(x), x.shape[0], x.shape[1], x.stride(0), axis,
+                                        ctypes.byref(d), _ptr(out), _stream(x.device))
+    _check(st, "ufp4_quant_stats_noalloc")
     return _stats_dict(out)
 
 
