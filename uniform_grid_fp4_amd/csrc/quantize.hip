@@ -164,7 +164,9 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Prefix sums of the groups' padded lengths into LDS (block-wide scan).
+// Prefix sums of the groups' padded lengths into LDS (block-wide scan over
+// NT threads).
+template <int NT = 256>
 __device__ __forceinline__ void load_group_tables(const int64_t *__restrict__ goff,
                                                   int n_groups, int64_t n_rows,
                                                   int64_t *s_off, int64_t *s_poff,
@@ -181,7 +183,7 @@ __device__ __forceinline__ void load_group_tables(const int64_t *__restrict__ go
     return;
   }
   // each thread sums the padded counts of a contiguous run of groups
-  const int per = (n_groups + 255) / 256;
+  const int per = (n_groups + NT - 1) / NT;
   const int g0 = tid * per;
   int64_t local = 0;
   // offsets are clamped to [0, n_rows] so that no access leaves the input
@@ -194,8 +196,8 @@ __device__ __forceinline__ void load_group_tables(const int64_t *__restrict__ go
   if (tid == 0) s_off[n_groups] = clamp_rows(goff[n_groups], n_rows);
   s_scan[tid] = local;
   __syncthreads();
-  // Hillis-Steele inclusive scan over 256 partial sums
-  for (int d = 1; d < 256; d <<= 1) {
+  // Hillis-Steele inclusive scan over NT partial sums
+  for (int d = 1; d < NT; d <<= 1) {
     const int64_t add = tid >= d ? s_scan[tid - d] : 0;
     __syncthreads();
     s_scan[tid] += add;
@@ -207,7 +209,7 @@ __device__ __forceinline__ void load_group_tables(const int64_t *__restrict__ go
     const int64_t cnt = s_off[g + 1] - s_off[g];
     run += (cnt > 0) ? (cnt + 15) / 16 * 16 : 0;
   }
-  if (tid == 255) s_poff[n_groups] = s_scan[255];
+  if (tid == NT - 1) s_poff[n_groups] = s_scan[NT - 1];
   __syncthreads();
 }
 
@@ -306,14 +308,26 @@ __device__ __forceinline__ int64_t xcd_major_block() {
 // Stacked mode (n_stack > 1, not GROUPED): the input rows are n_stack equal
 // groups of n_rows rows, each quantized on its own and written as output rows
 // [s * n_cols, (s + 1) * n_cols).
+// Threads per column-wise workgroup.  Wide RTNE tiles are shared by 8 waves
+// (each quantizes 2 of the 16 row-blocks): their LDS transpose tile (52 KiB)
+// then holds 8 waves instead of 4, so the VGPR budget (<= 128, 4 waves per
+// SIMD) rather than LDS bounds occupancy.  The stochastic-rounding kernels
+// need more registers (3 waves per SIMD) and keep 4 waves per tile.
+template <int CW, int RND>
+constexpr int col_threads() { return (CW == 4 && RND == kRoundRTNE) ? 512 : 256; }
+
 template <int GRID, int RND, bool RHT, bool VEC, bool GROUPED, int CW>
-__global__ __launch_bounds__(256) void quant_cols_kernel(
+__global__ __launch_bounds__((col_threads<CW, RND>())) void quant_cols_kernel(
     const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
     const int64_t *__restrict__ goff, int n_groups, int64_t n_stack, int64_t kpad,
     uint8_t *__restrict__ codes, float *__restrict__ scales, uint32_t sign_mask,
     uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id) {
   constexpr int kCols = 64 * CW;                 // tile columns
   constexpr int kTB = kColTileRows / 16;         // tile row-blocks
+  constexpr int kNT = col_threads<CW, RND>();    // threads: 4 or 8 waves share the tile
+  constexpr int kWaves = kNT / 64;
+  constexpr int kPerWave = kTB / kWaves;         // row-blocks per wave
+  static_assert(kPerWave * kWaves == kTB, "row-blocks per wave");
   // Narrow tiles prefetch the next row-block and walk down column strips;
   // wide ones hold twice the columns per lane, so they load one row-block at
   // a time (occupancy hides the latency) and interleave 4 row bands.
@@ -322,13 +336,13 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
   constexpr int kTabs = GROUPED ? kMaxGroups + 1 : 1;
   __shared__ int64_t s_off[kTabs];
   __shared__ int64_t s_poff[kTabs];
-  __shared__ int64_t s_scan[GROUPED ? 256 : 1];
+  __shared__ int64_t s_scan[GROUPED ? kNT : 1];
   __shared__ uint2 s_codes[kCols][kTB + 1];
   __shared__ float s_scales[kCols][kTB + 1];
 
   int64_t padded_end;
   if (GROUPED) {
-    load_group_tables(goff, n_groups, n_rows, s_off, s_poff, s_scan);
+    load_group_tables<kNT>(goff, n_groups, n_rows, s_off, s_poff, s_scan);
     padded_end = s_poff[n_groups];
   } else {
     padded_end = (n_rows + 15) / 16 * 16;
@@ -379,18 +393,18 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       keep[c] = (cc + 1 < n_cols) ? 0xFFFFFFFFu : (cc < n_cols ? 0x0000FFFFu : 0u);
     }
     const int colb = (int)(col * 2);
-    // Wave w quantizes row-blocks w, w+4, w+8, w+12 of the tile.
+    // Wave w quantizes row-blocks w, w + kWaves, ... of the tile.
     uint32_t cur[16][CW / 2], nxt[16][CW / 2];
     int64_t row0;
     int valid;
     block_rows(pb0 + wave, row0, valid);
     load_col_rows<VEC, CW>(xs, ld, n_cols, row0, valid, colb, keep, cur);
 #pragma unroll 1
-    for (int q = 0; q < 4; ++q) {
-      const int rb = wave + 4 * q;                    // block within the tile (wave-uniform)
+    for (int q = 0; q < kPerWave; ++q) {
+      const int rb = wave + kWaves * q;               // block within the tile (wave-uniform)
       const int64_t p = pb0 + rb;                     // padded block index
-      if (kPrefetch && q < 3) {
-        block_rows(p + 4, row0, valid);
+      if (kPrefetch && q < kPerWave - 1) {
+        block_rows(p + kWaves, row0, valid);
         load_col_rows<VEC, CW>(xs, ld, n_cols, row0, valid, colb, keep, nxt);
       }
 #pragma unroll
@@ -413,14 +427,14 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
         s_scales[CW * lane + 2 * c][rb] = sa;
         s_scales[CW * lane + 2 * c + 1][rb] = sb;
       }
-      if (q < 3) {
+      if (q < kPerWave - 1) {
         if (kPrefetch) {
 #pragma unroll
           for (int j = 0; j < 16; ++j)
 #pragma unroll
             for (int c = 0; c < CW / 2; ++c) cur[j][c] = nxt[j][c];
         } else {
-          block_rows(p + 4, row0, valid);
+          block_rows(p + kWaves, row0, valid);
           load_col_rows<VEC, CW>(xs, ld, n_cols, row0, valid, colb, keep, cur);
         }
       }
@@ -428,15 +442,16 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
     __syncthreads();
     // write back: kCols columns x 16 blocks of 8-byte codes; 16 consecutive
     // lanes write one column's 128 contiguous bytes
+    constexpr int kColStep = kNT / 16;                 // columns per pass
     const int nb = (int)((kblocks - pb0) < kTB ? (kblocks - pb0) : kTB);
     const int blk = tid & 15;
-    const int c0 = tid >> 4;                           // 0..15, then +16 per step
+    const int c0 = tid >> 4;                           // 0..kColStep-1, then +kColStep
     uint8_t *dq = codes + (out_row0 + col0 + c0) * (kpad / 2) + (pb0 + blk) * 8;
     float *ds = scales + (out_row0 + col0 + c0) * kblocks + pb0 + blk;
-    const int64_t step_q = 16 * (kpad / 2), step_s = 16 * kblocks;
+    const int64_t step_q = kColStep * (kpad / 2), step_s = kColStep * kblocks;
 #pragma unroll
-    for (int it = 0; it < kCols / 16; ++it) {
-      const int c = c0 + 16 * it;
+    for (int it = 0; it < kCols / kColStep; ++it) {
+      const int c = c0 + kColStep * it;
       if (col0 + c < n_cols && blk < nb) {
         // streaming stores: a later kernel reads the operand
         const uint2 cv = s_codes[c][blk];
@@ -773,7 +788,8 @@ static hipError_t launch_cols_cw(const QuantArgs &a, bool vec, hipStream_t st) {
   int blocks = grid_for(n_ptiles * n_ctiles * n_stack, 1, 256 * 16);
   if (blocks >= 8) blocks -= blocks % 8;   // whole XCD rounds (xcd_major_block)
 #define UFP4_QC(V, G)                                                                          \
-  hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, V, G, CW>), dim3(blocks), dim3(256), 0, \
+  hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, V, G, CW>), dim3(blocks),                \
+                     dim3(col_threads<CW, RND>()), 0,                                           \
                      st, a.x, rows_per, a.n_cols, a.ld, a.goff, a.n_groups, n_stack, a.kpad,    \
                      a.codes, a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id)
   const bool grouped = a.goff != nullptr;
