@@ -133,7 +133,12 @@ struct Gemm {
     rb_q = make_rsrc(g.b_codes + job.b_row0 * (g.kpad / 2), job.b_rows * (g.kpad / 2));
     rb_s = make_rsrc(g.b_scales + job.b_row0 * kblocks, job.b_rows * kblocks * 4);
     nkb = (int)(job.kb1 - job.kb0);
-    const int row = threadIdx.x >> kSBLog, blk = threadIdx.x & (kSB - 1);
+    int row = threadIdx.x >> kSBLog;
+    const int blk = threadIdx.x & (kSB - 1);
+    // opaque per tile: the lane's row offsets are formed here for every
+    // tile rather than hoisted out of the tile loop and held (spilled)
+    // across the K loop
+    asm volatile("" : "+v"(row));
     oq = (int)(row * (g.kpad / 2) + (job.kb0 + blk) * 8);
     os = (int)((row * kblocks + job.kb0 + blk) * 4);
   }
@@ -413,7 +418,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int64_t t_first = (MODE == 2) ? (int64_t)blockIdx.x
                                       : xcd * per + (int64_t)blockIdx.x / lanes;
 
-  for (int64_t t = t_first; t < t_end; t += t_step) {
+  const int64_t t_end_s = wave_uniform(t_end);
+  for (int64_t t = t_first;; t += t_step) {
+    // Loop-invariant 64-bit operands of the tile bookkeeping, made opaque per
+    // tile: the compares and the divisions below run on the vector unit, and
+    // hoisting their VGPR copies out of the loop would keep them live (and
+    // spilled) across the K loop.
+    int64_t kblocks_t = kblocks, tiles_n_t = tiles_n, t_end_t = t_end_s;
+    asm volatile("" : "+s"(kblocks_t), "+s"(tiles_n_t), "+s"(t_end_t));
+    if (t >= t_end_t) break;
     TileJob job;
     if (MODE == 0) {
       // split-K: tile t of split s covers blocks [s * split_kb, ...) and
@@ -425,13 +438,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         ++sp;
       }
       int64_t tm, tn;
-      band_tile(local, tiles_m, tiles_n, tm, tn);
+      band_tile(local, tiles_m, tiles_n_t, tm, tn);
       job.a_row0 = tm * kBM;
       job.a_rows = min((int64_t)kBM, g.M - job.a_row0);
       job.b_row0 = tn * kBN;
       job.b_rows = min((int64_t)kBN, g.N - job.b_row0);
-      job.kb0 = min(sp * g.split_kb, kblocks);
-      job.kb1 = min(job.kb0 + g.split_kb, kblocks);
+      job.kb0 = min(sp * g.split_kb, kblocks_t);
+      job.kb1 = min(job.kb0 + g.split_kb, kblocks_t);
       job.c_off = sp * g.split_stride + job.a_row0 * g.ldc + job.b_row0;
     } else if (MODE == 1) {
       int lo = 0, hi = g.n_groups;   // largest e with s_pre[e] <= t
@@ -442,7 +455,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       const int e = lo;
       const int64_t local = t - s_pre[e];
       int64_t tm, tn;
-      band_tile(local, (s_pre[e + 1] - s_pre[e]) / tiles_n, tiles_n, tm, tn);
+      band_tile(local, (s_pre[e + 1] - s_pre[e]) / tiles_n_t, tiles_n_t, tm, tn);
       job.a_row0 = s_off[e] + tm * kBM;
       job.a_rows = min((int64_t)kBM, s_off[e + 1] - job.a_row0);
       job.b_row0 = (int64_t)e * g.N + tn * kBN;
@@ -451,17 +464,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       job.kb1 = kblocks;
       job.c_off = job.a_row0 * g.ldc + tn * kBN;
     } else {
-      const int64_t per_group = tiles_m * tiles_n;
+      const int64_t per_group = tiles_m * tiles_n_t;
       const int64_t slot = t / per_group;
       const int64_t local = t - slot * per_group;
       const int64_t e = s_order[slot];
-      const int64_t tm = local / tiles_n, tn = local - tm * tiles_n;
+      const int64_t tm = local / tiles_n_t, tn = local - tm * tiles_n_t;
       job.a_row0 = tm * kBM;
       job.a_rows = min((int64_t)kBM, g.M - job.a_row0);
       job.b_row0 = tn * kBN;
       job.b_rows = min((int64_t)kBN, g.N - job.b_row0);
-      job.kb0 = min(s_pre[e] / 16, kblocks);
-      job.kb1 = min(s_pre[e + 1] / 16, kblocks);
+      job.kb0 = min(s_pre[e] / 16, kblocks_t);
+      job.kb1 = min(s_pre[e + 1] / 16, kblocks_t);
       job.c_off = e * g.M * g.ldc + job.a_row0 * g.ldc + job.b_row0;
     }
     if (MODE != 0) {

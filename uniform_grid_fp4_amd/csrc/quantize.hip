@@ -312,19 +312,23 @@ __device__ __forceinline__ int64_t xcd_major_block() {
 // (each quantizes 2 of the 16 row-blocks): their LDS transpose tile (52 KiB)
 // then holds 8 waves instead of 4, so the VGPR budget (<= 128, 4 waves per
 // SIMD) rather than LDS bounds occupancy.  The stochastic-rounding kernels
-// need more registers (3 waves per SIMD) and keep 4 waves per tile.
-template <int CW, int RND>
-constexpr int col_threads() { return (CW == 4 && RND == kRoundRTNE) ? 512 : 256; }
+// need more registers (3 waves per SIMD) and keep 4 waves per tile, and so
+// do the E2M1 grids, whose rounding is the longer instruction sequence (the
+// 8-wave tile measured 1.45x slower there).
+template <int GRID, int CW, int RND>
+constexpr int col_threads() {
+  return (GRID == kGridUniform && CW == 4 && RND == kRoundRTNE) ? 512 : 256;
+}
 
 template <int GRID, int RND, bool RHT, bool VEC, bool GROUPED, int CW>
-__global__ __launch_bounds__((col_threads<CW, RND>())) void quant_cols_kernel(
+__global__ __launch_bounds__((col_threads<GRID, CW, RND>())) void quant_cols_kernel(
     const uint16_t *__restrict__ x, int64_t n_rows, int64_t n_cols, int64_t ld,
     const int64_t *__restrict__ goff, int n_groups, int64_t n_stack, int64_t kpad,
     uint8_t *__restrict__ codes, float *__restrict__ scales, uint32_t sign_mask,
     uint32_t seed_lo, uint32_t seed_hi, uint32_t stream_id) {
   constexpr int kCols = 64 * CW;                 // tile columns
   constexpr int kTB = kColTileRows / 16;         // tile row-blocks
-  constexpr int kNT = col_threads<CW, RND>();    // threads: 4 or 8 waves share the tile
+  constexpr int kNT = col_threads<GRID, CW, RND>();  // threads: 4 or 8 waves share the tile
   constexpr int kWaves = kNT / 64;
   constexpr int kPerWave = kTB / kWaves;         // row-blocks per wave
   static_assert(kPerWave * kWaves == kTB, "row-blocks per wave");
@@ -789,7 +793,7 @@ static hipError_t launch_cols_cw(const QuantArgs &a, bool vec, hipStream_t st) {
   if (blocks >= 8) blocks -= blocks % 8;   // whole XCD rounds (xcd_major_block)
 #define UFP4_QC(V, G)                                                                          \
   hipLaunchKernelGGL((quant_cols_kernel<GRID, RND, RHT, V, G, CW>), dim3(blocks),                \
-                     dim3(col_threads<CW, RND>()), 0,                                           \
+                     dim3(col_threads<GRID, CW, RND>()), 0,                                      \
                      st, a.x, rows_per, a.n_cols, a.ld, a.goff, a.n_groups, n_stack, a.kpad,    \
                      a.codes, a.scales, a.sign_mask, a.seed_lo, a.seed_hi, a.stream_id)
   const bool grouped = a.goff != nullptr;
