@@ -62,9 +62,11 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # holds for the sources whose SHA-256 is recorded with it; after any change to
 # them the bench reports null until the counters are taken again.
 TRAFFIC = {
-    "dense-1.5B-fc1": {
-        "gemm": {"sha256": "971bca1c094a61516f3dc45f695bf48dbc823b70fd1cbf4105645979e74b7054",
-                 "bytes_per_launch": 361901606},
+    "moe-124B-experts-1gpu": {
+        "gemm": {"sha256": "fbfec17e7c4669882d53eac125d92a58c4a2596bf6ed2b4ea1991eedc0d8ab10",
+                 "bytes_per_launch": 31827163220},
+        "quantize": {"sha256": "d6e7163b87343605ff93b02c6cdfd2e42c6d7dc6ec65b148e45f61e772abfa17",
+                     "bytes_per_step": 17127793520},
     },
 }
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
@@ -115,12 +117,14 @@ def parse():
                     help="single: six single-axis quantizations per step; dual: three dual-axis "
                          "quantizations (one read of X, W and dY each, both operands out)")
     ap.add_argument("--workload", default="moe-124b",
-                    choices=["moe-124b", "dense-1.5b", "moe-7.9b", "quant-sweep", "copy",
-                             "q1-outputs", "mfma-peak"],
+                    choices=["moe-124b", "dense-1.5b", "moe-7.9b", "quant-sweep", "quant-2p28",
+                             "copy", "q1-outputs", "mfma-peak"],
                     help="moe-124b: the timed step on the MoE-124B expert layer, one GPU's "
                          "share (default); dense-1.5b, moe-7.9b: the same step on the dense "
                          "1.5B linear layer or the MoE-7.9B expert layer; quant-sweep: the "
-                         "2^28-element quantizer sweep, one JSON line per case; copy: a plain "
+                         "2^28-element quantizer sweep, one JSON line per case; quant-2p28: the "
+                         "UFP4 quantizer kernels alone on the sweep's Gaussian tensor (row- and "
+                         "column-wise, RTNE and SR, and dual-axis), back to back; copy: a plain "
                          "1 GiB device copy, the "
                          "streaming ceiling and the calibration run of the HBM traffic "
                          "counters; q1-outputs: GEMM-output SQNR of each recipe against the "
@@ -647,6 +651,52 @@ def mfma_peaks(args):
               flush=True)
 
 
+def quant_kernels(args):
+    """The UFP4 quantizer kernels on the 16384 x 16384 Gaussian sweep tensor
+    (uniform grid, RHT): row-wise and column-wise single-axis calls with RTNE
+    and SR, and the dual-axis call with RTNE and SR.  Each is timed with HIP
+    events over `steps` back-to-back calls after `warmup` (the 512 MiB input
+    streams from HBM every call); one JSON line per kernel, over the
+    algorithmic bytes (2.75 B per element per output, 2 B read once)."""
+    import torch
+    from uniform_grid_fp4_amd import ufp4 as U
+    from uniform_grid_fp4_amd import workloads as W
+    dev = torch.device("cuda:0")
+    x = W.sweep_tensor("gaussian", dev)
+    n = x.numel()
+    cases = [("rowwise", "rtne"), ("colwise-transposed", "rtne"), ("rowwise", "sr"),
+             ("colwise-transposed", "sr"), ("dual-axis", "rtne"), ("dual-axis", "sr")]
+    for layout, r in cases:
+        rnd = U.ROUND_SR if r == "sr" else U.ROUND_RTNE
+        if layout == "dual-axis":
+            sides = ((True, 0xBEEF, 0), (True, 0x1DEA, 1))
+            qr, qc = U.ufp4_rht_quantize_dual(x, *sides, rnd=rnd, seed=7)
+            call = lambda: U.ufp4_rht_quantize_dual(x, *sides, rnd=rnd, seed=7, out_rows=qr,
+                                                    out_cols=qc)
+            nbytes = n * BYTES_PER_DUAL_ELEM
+        else:
+            axis = U.BLOCKS_ALONG_COLS if layout == "rowwise" else U.BLOCKS_ALONG_ROWS
+            q = U.ufp4_rht_quantize(x, axis, True, 0xBEEF, U.GRID_UNIFORM, rnd, 7, 0)
+            call = lambda: U.ufp4_rht_quantize(x, axis, True, 0xBEEF, U.GRID_UNIFORM, rnd, 7, 0,
+                                               out=q)
+            nbytes = n * BYTES_PER_QUANT_ELEM
+        for _ in range(args.warmup):
+            call()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"workload": "quant-2p28", "layout": layout, "rounding": r,
+                          "grid": "uniform", "rht": True, "us": round(us, 2),
+                          "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}),
+              flush=True)
+
+
 def copy_ceiling(args):
     """A plain contiguous 1 GiB device-to-device copy (torch's copy kernel):
     the streaming ceiling the quantizer is compared with, and the run whose
@@ -681,6 +731,8 @@ def main():
         sys.exit(2)
     if args.workload == "quant-sweep":
         return quant_sweep(args)
+    if args.workload == "quant-2p28":
+        return quant_kernels(args)
     if args.workload == "copy":
         return copy_ceiling(args)
     if args.workload == "q1-outputs":
