@@ -64,9 +64,9 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 TRAFFIC = {
     "moe-124B-experts-1gpu": {
         "gemm": {"sha256": "fbfec17e7c4669882d53eac125d92a58c4a2596bf6ed2b4ea1991eedc0d8ab10",
-                 "bytes_per_launch": 31827163220},
+                 "bytes_per_launch": 22559742699},
         "quantize": {"sha256": "d6e7163b87343605ff93b02c6cdfd2e42c6d7dc6ec65b148e45f61e772abfa17",
-                     "bytes_per_step": 17127793520},
+                     "bytes_per_step": 16559008240},
     },
 }
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
