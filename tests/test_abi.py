@@ -291,3 +291,16 @@ def test_quant_stats_noalloc_rejects(kw, expect):
     a.update(kw)
     assert U.lib().ufp4_quant_stats_noalloc(a["x"], a["n_rows"], a["n_cols"], a["ld"], a["axis"],
                                             ctypes.byref(a["q"]), a["out"], None) == expect
+
+
+def test_grouped_capacity_rows_start_on_128_byte_boundaries():
+    """The binding's kpad for a grouped ALONG_ROWS output is at least the
+    call's minimum roundup16(rows + 15 * groups) and a multiple of 512, so
+    each output row's codes (kpad/2 bytes) and scales (kpad/4 bytes) start on
+    a 128-byte boundary; the MoE-124B tokens give 524800, not 524768."""
+    for rows, groups in ((524288, 32), (98304, 64), (1, 1), (255, 1), (256, 1), (4096, 1024)):
+        kp = U.padded_k_capacity(rows, groups)
+        minimum = (rows + 15 * groups + 15) // 16 * 16
+        assert kp >= minimum and kp - minimum < 512
+        assert kp % 512 == 0 and (kp // 2) % 128 == 0 and (kp // 16 * 4) % 128 == 0
+    assert U.padded_k_capacity(524288, 32) == 524800

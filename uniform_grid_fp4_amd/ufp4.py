@@ -133,11 +133,11 @@ class Quantized:
 def padded_k_capacity(n_rows: int, n_groups: int) -> int:
     """The kpad the binding gives a grouped ALONG_ROWS quantization: the
     smallest the call accepts, roundup16(n_rows + 15 * n_groups), rounded up
-    to a multiple of 256 so that every output row's codes (kpad/2 bytes) and
+    to a multiple of 512 so that every output row's codes (kpad/2 bytes) and
     scales (kpad/4 bytes) start on a 128-byte boundary.  Rows that do not
     (e.g. kpad = 524768 for the MoE-124B tokens) made the column-wise kernel's
     128-byte code pieces straddle two lines: 1.67x slower."""
-    return (n_rows + 15 * n_groups + 255) // 256 * 256
+    return (n_rows + 15 * n_groups + 511) // 512 * 512
 
 
 def _quant_shape(x: torch.Tensor, axis: int, group_offsets: Optional[torch.Tensor],
