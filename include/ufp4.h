@@ -139,8 +139,11 @@ typedef struct {
  *   to a multiple of 16 on its own, so no block straddles two groups, and
  *   group e occupies columns [P_e, P_{e+1}) of the output with
  *   P_e = sum_{e'<e} roundup16(count_e').  out->kpad must be at least
- *   roundup16(n_rows + 15*n_groups); columns from P_{n_groups} to kpad are
- *   written as zeros.  NULL means one group.  1 <= n_groups <= 1024.
+ *   roundup16(n_rows + 15*n_groups) and a multiple of 16 (a multiple of 512
+ *   keeps every output row 128-byte aligned, which the column-wise kernel
+ *   writes fastest); columns from P_{n_groups} to kpad are written as zeros.
+ *   NULL (n_groups 0) means one group with out->kpad = roundup16(n_rows)
+ *   exactly.  1 <= n_groups <= 1024.
  * rht, sign_mask: apply y = (1/4) H16 D x per block (butterfly stages
  *   h = 1,2,4,8 in FP32, then the exact 1/4) with D from the mask.
  * grid, rnd, seed, stream_id: see the enums above (seed/stream_id ignored
