@@ -63,17 +63,22 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # them the bench reports null until the counters are taken again.
 TRAFFIC = {
     "moe-124B-experts-1gpu": {
-        "gemm": {"sha256": "fbfec17e7c4669882d53eac125d92a58c4a2596bf6ed2b4ea1991eedc0d8ab10",
-                 "bytes_per_launch": 22559742699},
-        "quantize": {"sha256": "d6e7163b87343605ff93b02c6cdfd2e42c6d7dc6ec65b148e45f61e772abfa17",
-                     "bytes_per_step": 16559008240},
+        "gemm": {"sha256": "bf708a4bff38418a1c23711ad5262bbabe14d1a40836e81c41d69e6497c781be",
+                 "bytes_per_launch": 22869202964},
+        "quantize": {"sha256": "771515a38f55b326181985677210f6dc158637438cd7fec1e17e93c680ddaf78",
+                     "bytes_per_step": 16560323312},
     },
 }
+# The kernels, the host code that launches them and chooses split-K, the
+# binding that sets the output layouts (the grouped row length) and the
+# workload shapes: a change to any of them can change the bytes moved.
+_HOST_SOURCES = ("uniform_grid_fp4_amd/csrc/api.hip", "uniform_grid_fp4_amd/ufp4.py",
+                 "uniform_grid_fp4_amd/workloads.py")
 GEMM_SOURCES = ("uniform_grid_fp4_amd/csrc/gemm.hip", "uniform_grid_fp4_amd/csrc/ufp4_device.h",
-                "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
+                "uniform_grid_fp4_amd/csrc/ufp4_kernels.h") + _HOST_SOURCES
 QUANT_SOURCES = ("uniform_grid_fp4_amd/csrc/quantize.hip",
                  "uniform_grid_fp4_amd/csrc/ufp4_device.h",
-                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h")
+                 "uniform_grid_fp4_amd/csrc/ufp4_kernels.h") + _HOST_SOURCES
 MALL_BYTES = 256 << 20          # MI355X Infinity Cache
 
 
