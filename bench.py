@@ -64,9 +64,9 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 TRAFFIC = {
     "moe-124B-experts-1gpu": {
         "gemm": {"sha256": "bf708a4bff38418a1c23711ad5262bbabe14d1a40836e81c41d69e6497c781be",
-                 "bytes_per_launch": 22869202964},
-        "quantize": {"sha256": "771515a38f55b326181985677210f6dc158637438cd7fec1e17e93c680ddaf78",
-                     "bytes_per_step": 16560323312},
+                 "bytes_per_launch": 22281278866},
+        "quantize": {"sha256": "957ae19f262440f60093d60adeae28bb3d8e6e7b36aa80f0f4412cf50b6071a6",
+                     "bytes_per_step": 16554650417},
     },
 }
 # The kernels, the host code that launches them and chooses split-K, the
