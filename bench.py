@@ -64,9 +64,9 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 TRAFFIC = {
     "moe-124B-experts-1gpu": {
         "gemm": {"sha256": "bf708a4bff38418a1c23711ad5262bbabe14d1a40836e81c41d69e6497c781be",
-                 "bytes_per_launch": 22281278866},
-        "quantize": {"sha256": "957ae19f262440f60093d60adeae28bb3d8e6e7b36aa80f0f4412cf50b6071a6",
-                     "bytes_per_step": 16554650417},
+                 "bytes_per_launch": 22668941430},
+        "quantize": {"sha256": "b3abc9a1e774405ea6fd7c70796b1a163f2229e05912a74d97e85ddf7762160f",
+                     "bytes_per_step": 16587287985},
     },
 }
 # The kernels, the host code that launches them and chooses split-K, the
