@@ -63,10 +63,10 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # them the bench reports null until the counters are taken again.
 TRAFFIC = {
     "moe-124B-experts-1gpu": {
-        "gemm": {"sha256": "bf708a4bff38418a1c23711ad5262bbabe14d1a40836e81c41d69e6497c781be",
-                 "bytes_per_launch": 22668941430},
-        "quantize": {"sha256": "b3abc9a1e774405ea6fd7c70796b1a163f2229e05912a74d97e85ddf7762160f",
-                     "bytes_per_step": 16587287985},
+        "gemm": {"sha256": "54d42cd2232107c5af09ec684b9b6f34cfee6921b59d8f06714794d4cee8ff6c",
+                 "bytes_per_launch": 22513870508},
+        "quantize": {"sha256": "33d62ef7479b6da9e1db742fa2447191f5b916544f1ad67078f42b20bee7c1f0",
+                     "bytes_per_step": 16824376305},
     },
 }
 # The kernels, the host code that launches them and chooses split-K, the

@@ -567,7 +567,10 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const DualArgs a, int64
     valid = __builtin_amdgcn_readfirstlane(valid);
   };
 
-  for (int64_t tile_all = blockIdx.x; tile_all < total; tile_all += gridDim.x) {
+  // Each XCD takes a contiguous range of the row-band-major tile order (the
+  // launcher makes the grid a multiple of 8), so the tiles it runs together
+  // share input rows and output lines in its L2 (MoE-124B X: 3.18 -> 3.05 ms).
+  for (int64_t tile_all = xcd_major_block(); tile_all < total; tile_all += gridDim.x) {
     const int64_t si = tile_all / per_stack;
     const int64_t tile = tile_all - si * per_stack;
     const int64_t pt = tile / n_ctiles;
@@ -866,7 +869,8 @@ static hipError_t launch_dual_t(const DualArgs &a, hipStream_t st) {
   const int64_t n_ctiles = (a.n_cols + kColTileCols - 1) / kColTileCols;
   const int64_t n_stack = a.col_axis == 2 ? a.n_groups : 1;
   const int64_t rows_per = a.n_rows / n_stack;
-  const int blocks = grid_for(n_ptiles * n_ctiles * n_stack, 1, 256 * 8);
+  int blocks = grid_for(n_ptiles * n_ctiles * n_stack, 1, 256 * 8);
+  if (blocks >= 8) blocks -= blocks % 8;   // whole XCD rounds (xcd_major_block)
   const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0) &&
                    (a.n_cols % 2 == 0);
   const bool grouped = a.goff != nullptr;

@@ -232,11 +232,12 @@ __device__ __forceinline__ void quantize_block(float (&v)[16], uint64_t idx0, ui
         const float m = fabsf(th[j]);
         const uint32_t r = rnd[8 * h + j];
         if (GRID == kGridUniform) {
-          // k = floor(m) + (r < F), as an integer in byte 0 of floor(m) + 1.5*2^23
+          // k = floor(m) + (r < F); mc - floor(mc) is exact for 0 <= mc <= 7 and
+          // is what v_fract_f32 returns there, and the truncating conversion
+          // is floor(mc)
           const float mc = fminf(m, 7.0f);
-          const float fl = floorf(mc);
-          const uint32_t F = (uint32_t)((mc - fl) * 4294967296.0f);
-          k[j] = __float_as_uint(fl + 12582912.0f) + (r < F ? 1u : 0u);
+          const uint32_t F = (uint32_t)(__builtin_amdgcn_fractf(mc) * 4294967296.0f);
+          k[j] = (uint32_t)mc + (r < F ? 1u : 0u);
         } else {
           // m <= g up to one ulp; RTNE rounds that ulp back to g, SR must not
           // round past the top level
