@@ -211,7 +211,11 @@ ufp4_status ufp4_dequantize(const ufp4_qtensor *q, int32_t inverse_rht, float *o
  * transforms" and section 3.2).  All are C = A_hat * B_hat^T with both
  * operands K-contiguous ("TN"), FP32 out, row-major with stride ldc >= N:
  *   C[m, n] = sum_kb sa[m,kb] * sb[n,kb] * (sum_{k in kb} qa*qb) / g^2
- * over the operands' common kpad.  Operands must agree on k, kpad, grid, rht
+ * over the operands' common kpad.  Each block product is exact; the scale
+ * products and the sum over blocks are FP32, block by block, in chunks of
+ * 65536 K-elements whose partial results are added to C in chunk order (so
+ * the FP32 rounding error of the sum does not grow with kpad beyond one
+ * chunk's); results are deterministic.  Operands must agree on k, kpad, grid, rht
  * and sign_mask (else UFP4_ERR_MISMATCH), which is what makes the rotation
  * cancel.  All three grids are accepted; kpad > 2^24 returns
  * UFP4_ERR_UNSUPPORTED.
@@ -241,7 +245,10 @@ ufp4_status ufp4_gemm_wgrad(const ufp4_qtensor *dytq, const ufp4_qtensor *xtq, f
 /* Output element type of the GEMM calls with an out_dtype argument.
  *  F32:  the FP32 result, as the calls above write it.
  *  BF16: that FP32 result rounded to bf16, nearest even (bf16 bit patterns;
- *        the epilogue of a bf16 training step, half the output traffic). */
+ *        the epilogue of a bf16 training step, half the output traffic).
+ *        Past a chunk of 65536 K-elements the output holds the bf16 part of
+ *        the running result and the kernel keeps the rounding residual, so
+ *        the final value is the FP32 result rounded once more to bf16. */
 typedef enum { UFP4_OUT_F32 = 0, UFP4_OUT_BF16 = 1 } ufp4_out_dtype;
 
 /* ufp4_gemm_out -- FPROP (kind 0), DGRAD (1) or WGRAD (2) as above, with the

@@ -1,0 +1,137 @@
+"""Parity at the largest sizes the library accepts.
+
+* GEMMs at kpad = 2^24, the longest contraction the calls take (a 128-row
+  operand panel of 4-bit codes is then 2^30 bytes, inside the 32-bit buffer
+  offsets), dense (FPROP and split-K WGRAD) and K-grouped (WGRAD over three
+  token groups and an empty one, padded to exactly 2^24), on random codes and
+  scales: sampled outputs against the oracle's FP64 GEMM within
+  1e-5 * sum_k |a_k||b_k| (the GEMMs of paperlayer.ai summary section 2
+  "Random Hadamard transforms").  Once with random signs and once with every
+  product positive, where a single FP32 running sum over 2^20 blocks drifts
+  by about 1e-3 of the result: the kernels flush their FP32 sums to the
+  output every 65536 K-elements, which holds the error near 1e-7.
+* Column-wise (transposing) quantization of rows 2^26 elements long, the
+  largest row stride the call takes (16 rows then span 2^31 bytes): sampled
+  output rows against the oracle bit for bit (RTNE and SR), and the
+  dual-axis kernel's two outputs equal to the single-axis calls' whole
+  outputs."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ufp4_oracle as O
+from uniform_grid_fp4_amd import ufp4 as U
+from uniform_grid_fp4_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-5
+KMAX = 1 << 24
+LDMAX = 1 << 26
+MASK = 0x3C5A
+
+
+def random_operand(rows, kpad, seed, positive):
+    """Codes with every nibble drawn uniformly (sign bits cleared when
+    `positive`), scales 2^u with u uniform in [-6, 6)."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    codes = torch.randint(0, 256, (rows, kpad // 2), dtype=torch.uint8, device=DEV, generator=g)
+    if positive:
+        codes &= 0x77
+    u = torch.empty((rows, kpad // 16), dtype=torch.float32, device=DEV).uniform_(-6.0, 6.0,
+                                                                                  generator=g)
+    scales = torch.exp2(u)
+    return U.Quantized(codes, scales, rows, kpad, kpad, U.GRID_UNIFORM, 1, MASK)
+
+
+def host_rows(q, rows, k0=0, k1=None):
+    k1 = q.kpad if k1 is None else k1
+    return (q.codes[rows, k0 // 2:k1 // 2].cpu().numpy(),
+            q.scales[rows, k0 // 16:k1 // 16].cpu().numpy())
+
+
+def check(got, C, bound, what):
+    err = np.abs(got.astype(np.float64) - C)
+    lim = TOL * bound
+    assert (err <= lim).all(), f"{what}: worst err / bound = {(err / bound).max():.3g}"
+
+
+@pytest.mark.parametrize("positive", [False, True])
+def test_dense_gemm_at_the_largest_kpad(positive):
+    M, N = 160, 136
+    print(f"[maxsize] dense kpad=2^24 M={M} N={N} positive={positive}", flush=True)
+    a = random_operand(M, KMAX, 101, positive)
+    b = random_operand(N, KMAX, 102, positive)
+    fprop = U.ufp4_gemm_fprop(a, b)
+    need = U.ufp4_workspace_size(U.WGRAD, M, N, KMAX)
+    assert need > 0
+    ws = torch.empty(need // 4, dtype=torch.float32, device=DEV)
+    split = U.ufp4_gemm_wgrad(a, b, workspace=ws)
+    torch.cuda.synchronize()
+    rows, cols = [0, 97, M - 1], [0, 64, N - 1]
+    ca, sa = host_rows(a, rows)
+    cb, sb = host_rows(b, cols)
+    C, bound = O.gemm_tn(ca, sa, cb, sb)
+    for name, out in (("fprop", fprop), ("split-K wgrad", split)):
+        got = out.cpu().numpy()[np.ix_(rows, cols)]
+        check(got, C, bound, name)
+
+
+def test_grouped_wgrad_at_the_largest_kpad():
+    """Token groups of 5000003, 0, 6999997 and 4777191 rows: padded to 16
+    each they fill kpad = 2^24 exactly; every product positive."""
+    M, N = 144, 130
+    counts = [5000003, 0, 6999997, 4777191]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    poff = O.padded_offsets(off)
+    assert poff[-1] == KMAX
+    print(f"[maxsize] grouped wgrad kpad=2^24 groups={counts}", flush=True)
+    a = random_operand(M, KMAX, 103, True)
+    b = random_operand(N, KMAX, 104, True)
+    dw = U.ufp4_grouped_gemm(U.WGRAD, torch.as_tensor(off, device=DEV), a, b)
+    torch.cuda.synchronize()
+    assert (dw[1] == 0).all()
+    rows, cols = [0, 77, M - 1], [0, 3, N - 1]
+    for e, c in enumerate(counts):
+        if c == 0:
+            continue
+        k0, k1 = int(poff[e]), int(poff[e + 1])
+        ca, sa = host_rows(a, rows, k0, k1)
+        cb, sb = host_rows(b, cols, k0, k1)
+        C, bound = O.gemm_tn(ca, sa, cb, sb)
+        check(dw[e].cpu().numpy()[np.ix_(rows, cols)], C, bound, f"group {e}")
+
+
+def oracle_cols(bits, cols, rnd, seed, sid):
+    """The oracle's column-wise quantization of the sampled input columns:
+    output rows `cols` (their SR indices too)."""
+    xb = O.to_blocked_rows(O.bf16_bits_to_f32(bits), O.AXIS_ROWS)
+    nib, s = O.quantize_blocked(xb, True, MASK, O.GRID_UNIFORM, rnd, seed, sid, row_ids=cols)
+    return O.pack_nibbles(nib), s
+
+
+@pytest.mark.parametrize("n_cols", [LDMAX, LDMAX - 1])
+def test_column_quantize_at_the_largest_row_length(n_cols):
+    """17 rows (a full block of 16 and a ragged one) of a row stride 2^26:
+    n_cols = 2^26 takes the 8-byte vector loads, 2^26 - 1 the 2-byte ones."""
+    print(f"[maxsize] column-wise quantization ld=2^26 n_cols={n_cols}", flush=True)
+    full = W.bf16(W.normal((17, LDMAX), 1.0, 105, DEV))
+    x = full[:, :n_cols]
+    cols = np.array([0, 1, 2, 3, 1000003, (1 << 25) + 17, n_cols - 4, n_cols - 3, n_cols - 2,
+                     n_cols - 1], dtype=np.int64)
+    bits = W.bits_numpy(x[:, torch.as_tensor(cols, device=DEV)])
+    seed = 909
+    for rnd in (U.ROUND_RTNE, U.ROUND_SR):
+        cq = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_ROWS, True, MASK, U.GRID_UNIFORM, rnd, seed, 1)
+        torch.cuda.synchronize()
+        codes, scales = oracle_cols(bits, cols, rnd, seed, 1)
+        assert np.array_equal(cq.codes[cols].cpu().numpy(), codes), rnd
+        assert np.array_equal(cq.scales[cols].cpu().numpy().view(np.uint32),
+                              scales.view(np.uint32)), rnd
+        rq = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_COLS, True, 0x0F0F, U.GRID_UNIFORM, rnd, seed, 0)
+        dr, dc = U.ufp4_rht_quantize_dual(x, (True, 0x0F0F, 0), (True, MASK, 1), rnd=rnd,
+                                          seed=seed)
+        torch.cuda.synchronize()
+        assert torch.equal(dc.codes, cq.codes) and torch.equal(dc.scales, cq.scales), rnd
+        assert torch.equal(dr.codes, rq.codes) and torch.equal(dr.scales, rq.scales), rnd
+        del cq, rq, dr, dc

@@ -43,7 +43,11 @@
 // all their products in registers.
 // Tiles are assigned XCD-major: the 8 XCDs each walk a contiguous range of
 // tiles, so a row panel of A stays in one L2.  Outputs are written with
-// nontemporal (streaming) stores: nothing in the kernel reads them back.
+// nontemporal (streaming) stores.  A contraction longer than 65536 elements
+// is accumulated in chunks of that length: at the end of each chunk the
+// tile's FP32 sums are added to its outputs (read back by the same lanes),
+// so the error of the FP32 running sum stays that of a 65536-long chain
+// whatever K is; shorter contractions write once and are unchanged.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,6 +76,12 @@ static_assert((1 << kSBLog) == kSB, "kSBLog");
 static_assert(kAItems == 1 && kBItems == 1, "one A and one B staging item per thread");
 constexpr int kMaxGemmGroups = 1024;
 constexpr int kXcds = 8;
+// A tile's FP32 running sums go to its outputs every kFlushStages stages
+// (65536 K-elements): one FP32 chain over 2^20 blocks of same-signed
+// products drifts by about 1e-3 of the result, chunks of 4096 blocks by
+// about 1e-7.
+constexpr int kFlushStages = 1024;
+static_assert((kFlushStages & (kFlushStages - 1)) == 0 && kFlushStages % 2 == 0, "flush");
 
 struct Stage {
   uint8_t a[kBM * kRowBytes];
@@ -229,44 +239,65 @@ struct Gemm {
       for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
     const int nst = (nkb + kSB - 1) / kSB;
-    if (nst > 0) {
+    bool flushed = false;
+    // chunks of kFlushStages stages, each a full pipeline (its first stage
+    // staged before the loop); the last barrier of a chunk's loop comes
+    // after every wave's last read of both LDS buffers
+    for (int c0 = 0; c0 < nst; c0 += kFlushStages) {
+      const int c1 = min(nst, c0 + kFlushStages);
       Regs r;
-      load(r, 0);
+      load(r, c0);
       store(r, stages[0]);
       __syncthreads();
       // unrolled by two so that each half addresses its LDS buffer with
       // constant offsets
-      for (int st = 0; st < nst; st += 2) {
-        if (st + 1 < nst) load(r, st + 1);
+      for (int st = c0; st < c1; st += 2) {
+        if (st + 1 < c1) load(r, st + 1);
         compute(stages[0], acc);
-        if (st + 1 < nst) store(r, stages[1]);
+        if (st + 1 < c1) store(r, stages[1]);
         __syncthreads();
-        if (st + 1 >= nst) break;
-        if (st + 2 < nst) load(r, st + 2);
+        if (st + 1 >= c1) break;
+        if (st + 2 < c1) load(r, st + 2);
         compute(stages[1], acc);
-        if (st + 2 < nst) store(r, stages[0]);
+        if (st + 2 < c1) store(r, stages[0]);
         __syncthreads();
       }
+      if (c1 < nst) {
+        put<true>(acc, flushed);
+        flushed = true;
+      }
     }
+    put<false>(acc, flushed);
+  }
+
+  // Writes acc / g^2 to the tile's outputs, or adds it to what an earlier
+  // flush left there.  FLUSH (a chunk of a long contraction is done): acc
+  // then keeps what the output could not hold -- nothing for FP32 outputs,
+  // the bf16 rounding residual for bf16 outputs (exact in FP32, scaled back
+  // by g^2) -- and the next chunk accumulates on top of it.
+  template <bool FLUSH>
+  __device__ __forceinline__ void put(floatx16 (&acc)[kNT], bool add) {
     // 1/g^2, with the E2M1 levels doubled in FP8: 1/(2*6)^2 and 1/(2*2)^2
-    constexpr float inv_g2 = (GRID == kGridUniform) ? (1.0f / 49.0f)
-                             : (GRID == kGridE2M1) ? (1.0f / 144.0f) : (1.0f / 16.0f);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    constexpr float g2 = (GRID == kGridUniform) ? 49.0f : (GRID == kGridE2M1) ? 144.0f : 16.0f;
+    constexpr float inv_g2 = 1.0f / g2;
+    // Row offsets r -> 8*(r/4) + (r%4) are wave-uniform, so the per-lane part
+    // is one pointer and one remaining-rows count.  The tile's bookkeeping
+    // goes through empty asms so that the pointer and the sixteen row
+    // offsets are formed here, at each flush and after the K loop, instead
+    // of being hoisted and held in registers across it.
+    int tid = threadIdx.x;
+    int64_t ldc = g.ldc, c_off = job.c_off, a_rows = job.a_rows, b_rows = job.b_rows;
+    asm volatile("" : "+v"(tid), "+s"(ldc), "+s"(c_off), "+s"(a_rows), "+s"(b_rows));
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int wm = wave % kWavesM, wn = wave / kWavesM;
     const int l32 = lane & 31;
     const int half = lane >> 5;
-    // Row offsets r -> 8*(r/4) + (r%4) are wave-uniform, so the per-lane part
-    // is one pointer and one remaining-rows count.  ldc goes through an empty
-    // asm so that the sixteen row offsets are formed here, after the K loop,
-    // instead of being hoisted and held in registers across it.
-    int64_t ldc = g.ldc;
-    asm volatile("" : "+s"(ldc));
     const int m0 = wm * 32 + 4 * half;
     const int n0 = wn * kNT * 32 + l32;
-    const int mrem = (int)job.a_rows - m0;
-    const int nrem = (int)job.b_rows - n0;
-    const int64_t off = job.c_off + m0 * ldc + n0;
+    const int mrem = (int)a_rows - m0;
+    const int nrem = (int)b_rows - n0;
+    const int64_t off = c_off + m0 * ldc + n0;
     if (g.out_bf16) {
       // bf16 epilogue: the FP32 result rounded to nearest even (the bias
       // 0x7FFF + lsb carries into the kept half exactly when the dropped half
@@ -278,9 +309,13 @@ struct Gemm {
         for (int r = 0; r < 16; ++r) {
           const int dm = 8 * (r >> 2) + (r & 3);
           if (nt * 32 < nrem && dm < mrem) {
-            const uint32_t u = __float_as_uint(acc[nt][r] * inv_g2);
-            __builtin_nontemporal_store((uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16),
-                                        cl + dm * ldc + nt * 32);
+            uint16_t *p = cl + dm * ldc + nt * 32;
+            float t = acc[nt][r] * inv_g2;
+            if (add) t += __uint_as_float((uint32_t)*p << 16);
+            const uint32_t u = __float_as_uint(t);
+            const uint16_t h = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            __builtin_nontemporal_store(h, p);
+            if (FLUSH) acc[nt][r] = (t - __uint_as_float((uint32_t)h << 16)) * g2;
           }
         }
       }
@@ -291,8 +326,13 @@ struct Gemm {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int dm = 8 * (r >> 2) + (r & 3);
-          if (nt * 32 < nrem && dm < mrem)
-            __builtin_nontemporal_store(acc[nt][r] * inv_g2, cl + dm * ldc + nt * 32);
+          if (nt * 32 < nrem && dm < mrem) {
+            float *p = cl + dm * ldc + nt * 32;
+            float t = acc[nt][r] * inv_g2;
+            if (add) t += *p;
+            __builtin_nontemporal_store(t, p);
+          }
+          if (FLUSH) acc[nt][r] = 0.0f;
         }
       }
     }
