@@ -9,7 +9,9 @@
   "Random Hadamard transforms").  Once with random signs and once with every
   product positive, where a single FP32 running sum over 2^20 blocks drifts
   by about 1e-3 of the result: the kernels flush their FP32 sums to the
-  output every 65536 K-elements, which holds the error near 1e-7.
+  output every 65536 K-elements, which holds the error near 1e-7.  bf16
+  outputs of contractions several chunks long (dense and K-grouped) against
+  the oracle within the bar plus half a bf16 ulp.
 * Column-wise (transposing) quantization of rows 2^26 elements long, the
   largest row stride the call takes (16 rows then span 2^31 bytes): sampled
   output rows against the oracle bit for bit (RTNE and SR), and the
@@ -135,3 +137,54 @@ def test_column_quantize_at_the_largest_row_length(n_cols):
         assert torch.equal(dc.codes, cq.codes) and torch.equal(dc.scales, cq.scales), rnd
         assert torch.equal(dr.codes, rq.codes) and torch.equal(dr.scales, rq.scales), rnd
         del cq, rq, dr, dc
+
+
+def check_bf16(out, C, bound, what):
+    """bf16 output: the FP32 result within the bar, then rounded to bf16
+    (at most half a bf16 ulp, <= 2^-8 of the value)."""
+    o = out.float().cpu().numpy().astype(np.float64)
+    lim = TOL * bound + 2.0 ** -8 * (np.abs(C) + TOL * bound)
+    err = np.abs(o - C)
+    assert (err <= lim).all(), f"{what}: worst err / limit = {(err / lim).max():.3g}"
+
+
+def test_bf16_outputs_across_chunks():
+    """bf16 outputs of contractions several chunks long (the output holds the
+    bf16 part of the running result between chunks, the tile the residual):
+    a dense GEMM over 2^18 + 48 K-elements and a K-grouped WGRAD with groups
+    of 200003, 0 and 70001 tokens, every product positive; all outputs
+    against the oracle, and within one bf16 ulp of the FP32 output's
+    rounding."""
+    M, N, K = 96, 80, (1 << 18) + 48
+    print(f"[maxsize] bf16 outputs over {K} K-elements", flush=True)
+    a = random_operand(M, K, 111, True)
+    b = random_operand(N, K, 112, True)
+    bf = U.ufp4_gemm_out(U.WGRAD, a, b, dtype=torch.bfloat16)
+    f32 = U.ufp4_gemm_out(U.WGRAD, a, b, dtype=torch.float32)
+    torch.cuda.synchronize()
+    C, bound = O.gemm_tn(a.codes.cpu().numpy(), a.scales.cpu().numpy(), b.codes.cpu().numpy(),
+                         b.scales.cpu().numpy())
+    check(f32.cpu().numpy(), C, bound, "dense f32")
+    check_bf16(bf, C, bound, "dense bf16")
+    near = f32.to(torch.bfloat16).float()
+    assert ((bf.float() - near).abs() <= 2.0 ** -7 * near.abs()).all()
+
+    counts = [200003, 0, 70001]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    poff = O.padded_offsets(off)
+    kp = int(poff[-1])
+    ga = random_operand(M, kp, 113, True)
+    gb = random_operand(N, kp, 114, True)
+    offd = torch.as_tensor(off, device=DEV)
+    gbf = U.ufp4_grouped_gemm_out(U.WGRAD, offd, ga, gb, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert (gbf[1] == 0).all()
+    for e, c in enumerate(counts):
+        if c == 0:
+            continue
+        k0, k1 = int(poff[e]), int(poff[e + 1])
+        C, bound = O.gemm_tn(ga.codes[:, k0 // 2:k1 // 2].cpu().numpy(),
+                             ga.scales[:, k0 // 16:k1 // 16].cpu().numpy(),
+                             gb.codes[:, k0 // 2:k1 // 2].cpu().numpy(),
+                             gb.scales[:, k0 // 16:k1 // 16].cpu().numpy())
+        check_bf16(gbf[e], C, bound, f"grouped bf16 group {e}")
