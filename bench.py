@@ -63,10 +63,10 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 # them the bench reports null until the counters are taken again.
 TRAFFIC = {
     "moe-124B-experts-1gpu": {
-        "gemm": {"sha256": "54d42cd2232107c5af09ec684b9b6f34cfee6921b59d8f06714794d4cee8ff6c",
-                 "bytes_per_launch": 22513870508},
+        "gemm": {"sha256": "b3756901f52a1a4c3c0785f07446f908dc12bacf7b04ccc17bb3e0d119e6a19f",
+                 "bytes_per_launch": 22680509016},
         "quantize": {"sha256": "33d62ef7479b6da9e1db742fa2447191f5b916544f1ad67078f42b20bee7c1f0",
-                     "bytes_per_step": 16824376305},
+                     "bytes_per_step": 16819665425},
     },
 }
 # The kernels, the host code that launches them and chooses split-K, the
