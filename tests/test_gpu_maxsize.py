@@ -188,3 +188,68 @@ def test_bf16_outputs_across_chunks():
                              gb.codes[:, k0 // 2:k1 // 2].cpu().numpy(),
                              gb.scales[:, k0 // 16:k1 // 16].cpu().numpy())
         check_bf16(gbf[e], C, bound, f"grouped bf16 group {e}")
+
+
+def gemm_bound_check(got, C, bound, what):
+    err = np.abs(got.astype(np.float64) - C)
+    bad = err > TOL * bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} outside"
+
+
+def test_grouped_at_the_largest_group_count():
+    """1024 expert groups, the calls' limit (the GEMMs' and quantizers' group
+    tables; above 256 groups the K-grouped WGRAD takes its groups in index
+    order instead of heaviest first): counts 0..6 with every fifth group
+    empty, so most groups are shorter than a 16-row block.  Grouped
+    quantizations (single-axis, stacked and dual-axis) bit-exact against the
+    oracle, and FPROP, DGRAD and WGRAD on them element by element."""
+    E, H, F = 1024, 48, 32
+    counts = np.random.default_rng(7).integers(0, 7, size=E)
+    counts[::5] = 0
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(off[-1])
+    print(f"[maxsize] {E} groups, {T} rows", flush=True)
+    offd = torch.as_tensor(off, device=DEV)
+    x = W.bf16(W.normal((T, H), 1.0, 120, DEV))
+    w = W.bf16(W.normal((E * F, H), 0.02, 121, DEV))
+    dy = W.bf16(W.normal((T, F), 1e-4, 122, DEV))
+    m1, m2, m3, seed = 0x1F2E, 0x3D4C, 0x5B6A, 55
+    xb, wb, gb = W.bits_numpy(x), W.bits_numpy(w), W.bits_numpy(dy)
+    host = lambda t: t.cpu().numpy()
+
+    def same(q, ref, what):
+        codes, scales, _ = ref
+        assert np.array_equal(host(q.codes), codes), what
+        assert np.array_equal(host(q.scales).view(np.uint32), scales.view(np.uint32)), what
+
+    xq = U.ufp4_rht_quantize(x, U.BLOCKS_ALONG_COLS, True, m1)
+    wq = U.ufp4_rht_quantize(w, U.BLOCKS_ALONG_COLS, True, m1)
+    wtq = U.ufp4_rht_quantize(w, U.BLOCKS_ALONG_ROWS_STACKED, True, m2, n_groups=E)
+    dyq = U.ufp4_rht_quantize(dy, U.BLOCKS_ALONG_COLS, True, m2, rnd=U.ROUND_SR, seed=seed)
+    dq, dtq = U.ufp4_rht_quantize_dual(dy, (True, m2, 0), (True, m3, 1), rnd=U.ROUND_SR,
+                                       seed=seed, group_offsets=offd)
+    _, xtq = U.ufp4_rht_quantize_dual(x, (True, m1, 0), (True, m3, 0), group_offsets=offd)
+    torch.cuda.synchronize()
+    assert torch.equal(dq.codes, dyq.codes) and torch.equal(dq.scales, dyq.scales)
+    kp = dtq.kpad
+    same(wtq, O.quantize(wb, O.AXIS_ROWS_STACKED, True, m2, O.GRID_UNIFORM, 0, n_stack=E),
+         "stacked W^T")
+    same(dtq, O.quantize(gb, O.AXIS_ROWS, True, m3, O.GRID_UNIFORM, 1, seed, 1, group_offsets=off,
+                         kpad=kp), "grouped dY^T")
+    same(xtq, O.quantize(xb, O.AXIS_ROWS, True, m3, O.GRID_UNIFORM, 0, group_offsets=off,
+                         kpad=kp), "grouped X^T")
+
+    y = U.ufp4_grouped_gemm(U.FPROP, offd, xq, wq)
+    dx = U.ufp4_grouped_gemm(U.DGRAD, offd, dyq, wtq)
+    dw = U.ufp4_grouped_gemm(U.WGRAD, offd, dtq, xtq)
+    torch.cuda.synchronize()
+    C, bnd = O.grouped_gemm(0, off, host(xq.codes), host(xq.scales), host(wq.codes),
+                            host(wq.scales), F)
+    gemm_bound_check(host(y), C, bnd, "fprop")
+    C, bnd = O.grouped_gemm(1, off, host(dyq.codes), host(dyq.scales), host(wtq.codes),
+                            host(wtq.scales), H)
+    gemm_bound_check(host(dx), C, bnd, "dgrad")
+    C, bnd = O.grouped_gemm(2, off, host(dtq.codes), host(dtq.scales), host(xtq.codes),
+                            host(xtq.scales), 0)
+    gemm_bound_check(host(dw), C, bnd, "wgrad")
+    assert (host(dw)[counts == 0] == 0).all()
