@@ -16,7 +16,9 @@
   largest row stride the call takes (16 rows then span 2^31 bytes): sampled
   output rows against the oracle bit for bit (RTNE and SR), and the
   dual-axis kernel's two outputs equal to the single-axis calls' whole
-  outputs."""
+  outputs.
+* 1024 expert groups, the largest group count the grouped calls take
+  (quantizations and GEMMs), most of them empty or shorter than a block."""
 import numpy as np
 import pytest
 import torch
