@@ -254,7 +254,7 @@ typedef enum { UFP4_OUT_F32 = 0, UFP4_OUT_BF16 = 1 } ufp4_out_dtype;
 /* ufp4_gemm_out -- FPROP (kind 0), DGRAD (1) or WGRAD (2) as above, with the
  * output element type chosen by out_dtype (ldc in elements).  c must be
  * aligned to its element size.  Returns OK, INVALID_ARG, SHAPE, MISMATCH,
- * HIP. */
+ * UNSUPPORTED, HIP. */
 ufp4_status ufp4_gemm_out(int32_t kind, const ufp4_qtensor *a, const ufp4_qtensor *b, void *c,
                           int32_t out_dtype, int64_t ldc, hipStream_t stream);
 
@@ -272,9 +272,12 @@ ufp4_status ufp4_gemm_out(int32_t kind, const ufp4_qtensor *a, const ufp4_qtenso
  *   quantized ALONG_ROWS with the same offsets (per-group padding, see
  *   ufp4_rht_quantize); C is [n_groups, M, N] with group stride M*ldc, and an
  *   empty group writes zeros.
+ * 1 <= n_groups <= 1024 (else SHAPE); kpad > 2^24 returns UNSUPPORTED, and
+ * the sums are accumulated as for the dense calls.
  * The grouped forms never split K (their per-group tiles fill the GPU), so
  * the workspace is unused: pass NULL and 0 (a non-NULL workspace with a size
- * is accepted and ignored).  Returns OK, INVALID_ARG, SHAPE, MISMATCH, HIP. */
+ * is accepted and ignored).  Returns OK, INVALID_ARG, SHAPE, MISMATCH,
+ * UNSUPPORTED, HIP. */
 ufp4_status ufp4_grouped_gemm(int32_t kind, int32_t n_groups, const int64_t *d_group_offsets,
                               const ufp4_qtensor *a, const ufp4_qtensor *b, float *c,
                               int64_t ldc, void *workspace, size_t workspace_bytes,

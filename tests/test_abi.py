@@ -239,6 +239,19 @@ def test_size_limits_of_32_bit_offsets():
     assert quant(axis=1, ld=(1 << 26) + 2, out=fake_desc(rows=32, kpad=32)) == -4
     big = fake_desc(k=(1 << 24) + 16, kpad=(1 << 24) + 16)
     assert gemm(U.lib().ufp4_gemm_fprop, big, big) == -4
+    L = U.lib()
+    assert L.ufp4_gemm_out(0, ctypes.byref(big), ctypes.byref(big), FAKE, 1, 32, None) == -4
+    for kind in (0, 1, 2):
+        assert L.ufp4_grouped_gemm(kind, 2, FAKE, ctypes.byref(big), ctypes.byref(big), FAKE, 32,
+                                   None, 0, None) == -4
+        assert L.ufp4_grouped_gemm_out(kind, 2, FAKE, ctypes.byref(big), ctypes.byref(big), FAKE,
+                                       0, 32, None) == -4
+    # at most 1024 groups
+    ok = fake_desc()
+    assert L.ufp4_grouped_gemm(0, 1025, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 32, None,
+                               0, None) == -2
+    assert L.ufp4_grouped_gemm_out(2, 1025, FAKE, ctypes.byref(ok), ctypes.byref(ok), FAKE, 0, 32,
+                                   None) == -2
 
 
 def test_workspace_size_splits_long_k_of_small_outputs():
