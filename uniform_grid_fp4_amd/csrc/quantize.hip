@@ -517,10 +517,14 @@ __device__ __forceinline__ void unpack_block(const uint4 a0, const uint4 a1, uin
 template <int GRID, int RND, bool VEC, bool GROUPED>
 __global__ __launch_bounds__(256) void quant_dual_kernel(const DualArgs a, int64_t n_rows,
                                                          int64_t n_stack) {
-  constexpr int kTabs = GROUPED ? kMaxGroups + 1 : 1;
   constexpr int kTrStride = 68;                     // dwords per staged row (64 + 4 pad)
-  __shared__ int64_t s_off[kTabs];
-  __shared__ int64_t s_poff[kTabs];
+  // Grouped: the group tables, n_groups + 1 entries each, in dynamic LDS
+  // sized by the launch, so that a few groups leave room for three
+  // workgroups per CU (the occupancy registers allow) where tables for the
+  // 1024-group maximum would leave two.
+  extern __shared__ int64_t s_tabs[];
+  int64_t *const s_off = s_tabs;
+  int64_t *const s_poff = s_tabs + (a.n_groups + 1);
   __shared__ int64_t s_scan[GROUPED ? 256 : 1];
   __shared__ uint2 s_codes[kColTileCols][kColTileRows / 16 + 1];
   __shared__ float s_scales[kColTileCols][kColTileRows / 16 + 1];
@@ -874,8 +878,11 @@ static hipError_t launch_dual_t(const DualArgs &a, hipStream_t st) {
   const bool vec = ((reinterpret_cast<uintptr_t>(a.x) & 3u) == 0) && (a.ld % 2 == 0) &&
                    (a.n_cols % 2 == 0);
   const bool grouped = a.goff != nullptr;
+  // the group tables' dynamic LDS (at most 16.4 KB: with the static 45.5 KB
+  // the workgroup stays within 64 KB)
+  const size_t tabs = grouped ? 2 * (size_t)(a.n_groups + 1) * sizeof(int64_t) : 0;
 #define UFP4_QD(V, G) \
-  hipLaunchKernelGGL((quant_dual_kernel<GRID, RND, V, G>), dim3(blocks), dim3(256), 0, st, a, \
+  hipLaunchKernelGGL((quant_dual_kernel<GRID, RND, V, G>), dim3(blocks), dim3(256), tabs, st, a, \
                      rows_per, n_stack)
   if (vec) {
     if (grouped) UFP4_QD(true, true); else UFP4_QD(true, false);
