@@ -64,9 +64,9 @@ BYTES_PER_DUAL_ELEM = 2.0 + 2 * (0.5 + 0.25)
 TRAFFIC = {
     "moe-124B-experts-1gpu": {
         "gemm": {"sha256": "b3756901f52a1a4c3c0785f07446f908dc12bacf7b04ccc17bb3e0d119e6a19f",
-                 "bytes_per_launch": 22680509016},
-        "quantize": {"sha256": "33d62ef7479b6da9e1db742fa2447191f5b916544f1ad67078f42b20bee7c1f0",
-                     "bytes_per_step": 16819665425},
+                 "bytes_per_launch": 22459143930},
+        "quantize": {"sha256": "9bc2220e9251f951c8558751186c15ffbc050a44615921d8983718693798e53f",
+                     "bytes_per_step": 16904243057},
     },
 }
 # The kernels, the host code that launches them and chooses split-K, the
