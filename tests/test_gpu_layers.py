@@ -6,7 +6,9 @@ SR seed, then its FP64 GEMMs: |out - C| <= 1e-5 * sum_k |a_k||b_k| plus half a
 bf16 ulp of the output for the epilogue's rounding), and stay within 4-bit
 quantization noise of the unquantized product.  The recipe the layers follow
 is the paperlayer.ai summary's section 4 "UFP4 Recipe" (RHT on all three
-GEMMs along their contraction dimensions, stochastic rounding on dY only)."""
+GEMMs along their contraction dimensions, stochastic rounding on dY only);
+its section 5 "Q4" ablations (RHT on a subset of the GEMMs, dY without SR)
+are layer options checked the same way."""
 import numpy as np
 import pytest
 import torch
@@ -33,19 +35,21 @@ def assert_bf16_close(out, C, bound, what):
                            f"{(err / np.maximum(lim, 1e-300)).max():.3g}")
 
 
-def oracle_linear(x, w, g, masks, seed, grid=O.GRID_UNIFORM):
+def oracle_linear(x, w, g, masks, seed, grid=O.GRID_UNIFORM, rht=(True, True, True), rnd_dy=1):
     """The oracle's three GEMMs of a linear layer: the six quantized operands
-    (X and W along H, dY along F with SR stream 0, W^T along F, dY^T with SR
-    stream 1 and X^T along the tokens) and FP64 products."""
+    (X and W along H, dY along F with stream 0, W^T along F, dY^T with stream
+    1 and X^T along the tokens; each GEMM's pair with its RHT flag, dY with
+    rounding rnd_dy) and FP64 products."""
     mf, md, mw = masks
+    rf, rd, rw = rht
     xb, wb, gb = W.bits_numpy(x), W.bits_numpy(w), W.bits_numpy(g)
-    q = lambda b, axis, mask, rnd=0, sid=0: O.quantize(b, axis, True, mask, grid, rnd, seed, sid)
-    cx, sx, _ = q(xb, O.AXIS_COLS, mf)
-    cw, sw, _ = q(wb, O.AXIS_COLS, mf)
-    cg, sg, _ = q(gb, O.AXIS_COLS, md, 1, 0)
-    cwt, swt, _ = q(wb, O.AXIS_ROWS, md)
-    cgt, sgt, _ = q(gb, O.AXIS_ROWS, mw, 1, 1)
-    cxt, sxt, _ = q(xb, O.AXIS_ROWS, mw)
+    q = lambda b, axis, r, mask, rnd=0, sid=0: O.quantize(b, axis, r, mask, grid, rnd, seed, sid)
+    cx, sx, _ = q(xb, O.AXIS_COLS, rf, mf)
+    cw, sw, _ = q(wb, O.AXIS_COLS, rf, mf)
+    cg, sg, _ = q(gb, O.AXIS_COLS, rd, md, rnd_dy, 0)
+    cwt, swt, _ = q(wb, O.AXIS_ROWS, rd, md)
+    cgt, sgt, _ = q(gb, O.AXIS_ROWS, rw, mw, rnd_dy, 1)
+    cxt, sxt, _ = q(xb, O.AXIS_ROWS, rw, mw)
     return (O.gemm_tn(cx, sx, cw, sw, grid), O.gemm_tn(cg, sg, cwt, swt, grid),
             O.gemm_tn(cgt, sgt, cxt, sxt, grid))
 
@@ -150,3 +154,71 @@ def test_expert_layer():
         if counts[e] >= 16:
             assert rel_rms(x.grad[o[e]:o[e + 1]], ge @ we) < 0.3
             assert rel_rms(layer.weight.grad[e * F:(e + 1) * F], ge.t() @ xe) < 0.3
+
+
+@pytest.mark.parametrize("rht,sr_dy", [((False, False, True), True), ((True, False, True), True),
+                                       ((False, True, True), True), ((True, True, True), False),
+                                       ((False, False, False), False)])
+def test_linear_layer_recipe_ablations(rht, sr_dy):
+    """The recipe ablations of the paperlayer.ai summary, section 5 "Q4":
+    RHT on WGRAD only, on FPROP and WGRAD, on DGRAD and WGRAD, full RHT
+    without SR on dY, and neither.  Each GEMM's operands carry that GEMM's
+    flag; forward and both gradients equal the explicit C-ABI sequence and
+    match the oracle element by element."""
+    torch.manual_seed(2)
+    layer = UFP4Linear(128, 96, seed=4, device=DEV, rht=rht, sr_dy=sr_dy)
+    x = torch.randn((80, 128), device=DEV).to(torch.bfloat16).requires_grad_(True)
+    g = torch.randn((80, 96), device=DEV).to(torch.bfloat16)
+    y = layer(x)
+    y.backward(g)
+    mf, md, mw = layer.masks
+    rf, rd, rw = rht
+    rnd = U.ROUND_SR if sr_dy else U.ROUND_RTNE
+    w = layer.weight.detach()
+    xq, xtq = U.ufp4_rht_quantize_dual(x.detach(), (rf, mf, 0), (rw, mw, 0))
+    wq, wtq = U.ufp4_rht_quantize_dual(w, (rf, mf, 0), (rd, md, 0))
+    dq, dtq = U.ufp4_rht_quantize_dual(g, (rd, md, 0), (rw, mw, 1), rnd=rnd, seed=layer.sr_seed)
+    assert (xq.rht, xtq.rht, dq.rht, dtq.rht) == (int(rf), int(rw), int(rd), int(rw))
+    assert torch.equal(y, U.ufp4_gemm_out(U.FPROP, xq, wq))
+    assert torch.equal(x.grad, U.ufp4_gemm_out(U.DGRAD, dq, wtq))
+    assert torch.equal(layer.weight.grad, U.ufp4_gemm_out(U.WGRAD, dtq, xtq))
+    (Cy, By), (Cdx, Bdx), (Cdw, Bdw) = oracle_linear(x.detach(), w, g, layer.masks,
+                                                     layer.sr_seed, rht=rht,
+                                                     rnd_dy=1 if sr_dy else 0)
+    assert_bf16_close(y, Cy, By, "fprop")
+    assert_bf16_close(x.grad, Cdx, Bdx, "dgrad")
+    assert_bf16_close(layer.weight.grad, Cdw, Bdw, "wgrad")
+
+
+def test_expert_layer_recipe_ablation():
+    """The expert layer with RHT on WGRAD only and round-to-nearest dY."""
+    torch.manual_seed(3)
+    counts = [30, 0, 50, 17]
+    E, H, F = len(counts), 64, 48
+    off = torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int64, device=DEV)
+    T = sum(counts)
+    layer = UFP4ExpertLinear(E, H, F, seed=6, device=DEV, rht=(False, False, True), sr_dy=False)
+    x = torch.randn((T, H), device=DEV).to(torch.bfloat16).requires_grad_(True)
+    g = torch.randn((T, F), device=DEV).to(torch.bfloat16)
+    y = layer(x, off)
+    y.backward(g)
+    mf, md, mw = layer.masks
+    o = off.tolist()
+    w = layer.weight.detach()
+    xb, wb, gb = W.bits_numpy(x.detach()), W.bits_numpy(w), W.bits_numpy(g)
+    grid = O.GRID_UNIFORM
+    kp = U.padded_k_capacity(T, E)
+    cx, sx, _ = O.quantize(xb, O.AXIS_COLS, False, mf, grid, 0)
+    cw, sw, _ = O.quantize(wb, O.AXIS_COLS, False, mf, grid, 0)
+    cg, sg, _ = O.quantize(gb, O.AXIS_COLS, False, md, grid, 0)
+    cwt, swt, _ = O.quantize(wb, O.AXIS_ROWS_STACKED, False, md, grid, 0, n_stack=E)
+    cgt, sgt, _ = O.quantize(gb, O.AXIS_ROWS, True, mw, grid, 0, layer.sr_seed, 1,
+                             group_offsets=o, kpad=kp)
+    cxt, sxt, _ = O.quantize(xb, O.AXIS_ROWS, True, mw, grid, 0, group_offsets=o, kpad=kp)
+    Cy, By = O.grouped_gemm(0, o, cx, sx, cw, sw, F, grid)
+    Cdx, Bdx = O.grouped_gemm(1, o, cg, sg, cwt, swt, H, grid)
+    Cdw, Bdw = O.grouped_gemm(2, o, cgt, sgt, cxt, sxt, H, grid)
+    assert_bf16_close(y, Cy, By, "expert fprop")
+    assert_bf16_close(x.grad, Cdx, Bdx, "expert dgrad")
+    assert_bf16_close(layer.weight.grad, Cdw.reshape(E * F, H), Bdw.reshape(E * F, H),
+                      "expert wgrad")
