@@ -10,8 +10,8 @@
   product positive, where a single FP32 running sum over 2^20 blocks drifts
   by about 1e-3 of the result: the kernels flush their FP32 sums to the
   output every 65536 K-elements, which holds the error near 1e-7.  bf16
-  outputs of contractions several chunks long (dense and K-grouped) against
-  the oracle within the bar plus half a bf16 ulp.
+  outputs of contractions several chunks long (dense, K-grouped and
+  M-grouped) against the oracle within the bar plus half a bf16 ulp.
 * Column-wise (transposing) quantization of rows 2^26 elements long, the
   largest row stride the call takes (16 rows then span 2^31 bytes): sampled
   output rows against the oracle bit for bit (RTNE and SR), and the
@@ -255,3 +255,23 @@ def test_grouped_at_the_largest_group_count():
                             host(xtq.scales), 0)
     gemm_bound_check(host(dw), C, bnd, "wgrad")
     assert (host(dw)[counts == 0] == 0).all()
+
+
+def test_m_grouped_gemm_across_chunks():
+    """Grouped FPROP (groups along M) over 2^17 + 16 K-elements, two chunks
+    and a remainder, every product positive: FP32 and bf16 outputs against
+    the oracle."""
+    counts = [70, 0, 200, 33]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T, E, N, K = int(off[-1]), len(counts), 72, (1 << 17) + 16
+    print(f"[maxsize] M-grouped FPROP over {K} K-elements", flush=True)
+    a = random_operand(T, K, 131, True)
+    b = random_operand(E * N, K, 132, True)
+    offd = torch.as_tensor(off, device=DEV)
+    f32 = U.ufp4_grouped_gemm(U.FPROP, offd, a, b)
+    bf = U.ufp4_grouped_gemm_out(U.FPROP, offd, a, b, torch.bfloat16)
+    torch.cuda.synchronize()
+    C, bound = O.grouped_gemm(0, off, a.codes.cpu().numpy(), a.scales.cpu().numpy(),
+                              b.codes.cpu().numpy(), b.scales.cpu().numpy(), N)
+    check(f32.cpu().numpy(), C, bound, "M-grouped f32")
+    check_bf16(bf, C, bound, "M-grouped bf16")
